@@ -1,0 +1,200 @@
+"""Plain CPU oracle for DDTree tree verification (test infrastructure only).
+
+This module is the correctness reference for the GPU library.  It is test
+infrastructure: only the test suite, the smoke check and the benchmark's CPU
+baseline leg import it.  The product path never calls it, and it shares no
+code with the HIP kernels or their host library.  Everything is computed in
+float64 with NumPy, in the most direct form of each definition: no online
+softmax, no tiling, no bitmask tricks beyond storing the mask.
+
+Pages cited (titles of the source pages):
+  [Validating] "The Moment of Proof: Validating a Native CUDA Speculative Decoding Engine"
+  [Running]    "The Moment of Proof: Running the Native DDTree Speculative Decoding Engine"
+  [Truth]      "The Moment of Truth: Validating a Custom CUDA Inference Engine for Kimi K2.6"
+  [Build]      "The Build That Proved It: Compiling the Native DDTree Speculative Decoding Engine"
+
+What the pages fix, and the readings taken where they are silent:
+  * A draft tree is verified in one target forward under a custom attention
+    mask; the accepted tokens are those on the longest path whose tokens match
+    the target's greedy choices ([Validating] "Input Knowledge Required";
+    [Running] "Input Knowledge Required"; [Build] "The Output Knowledge Created").
+  * The tree is a parent array, node 0 the root (the last committed token),
+    parent[i] < i.  A node sees the cached prefix plus its ancestors and
+    itself (reading: ancestor-or-self, so that a single chain is causal).
+  * Attention is MLA in absorbed form: scores use the latent query against
+    the latent cache row c plus the rotary query against the rotary key r;
+    the value is the latent row c itself ([Validating] "Input Knowledge
+    Required": the absorb form folds the up-projections into attention).
+  * Positions are cache length plus node depth, as int64 ([Build] "The
+    Thinking Process Visible in Reasoning").
+  * The log-sum-exp is the natural log of the sum of exp of the scaled scores.
+  * Greedy accept: a node's draft token is accepted when it equals the
+    target's argmax at its parent and its parent is accepted; the longest
+    accepted root path wins, ties to the smallest terminal index; the
+    commit is the path's draft tokens after the root plus the target's
+    argmax at the terminal node (the bonus token).  argmax ties go to the
+    lowest vocabulary index (NumPy's argmax).
+
+Every function here is pinned by the CPU tests against closed forms, special
+cases that reduce to library routines and brute-force alternatives.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["tree_is_valid", "build_mask_ref", "visible_nodes", "verify_attn_ref", "target_argmax_ref",
+           "greedy_accept_ref"]
+
+
+# ----------------------------------------------------------------------------
+# Visibility mask, depth and positions
+# ----------------------------------------------------------------------------
+
+def tree_is_valid(parent_row: np.ndarray) -> bool:
+    """Root first with parent -1, every other parent an earlier node."""
+    n = len(parent_row)
+    if n == 0 or int(parent_row[0]) != -1:
+        return False
+    return all(0 <= int(parent_row[i]) < i for i in range(1, n))
+
+
+def build_mask_ref(parents: np.ndarray, prefix_lens: np.ndarray | None = None):
+    """Ancestor-or-self visibility mask of every tree node, by pointer chasing.
+
+    The mask is the custom attention mask of tree verification ([Validating]
+    "Input Knowledge Required"; [Validating] "Output Knowledge Created":
+    attention mask construction in the live decode loop).  Node depth is the
+    number of parent steps to the root; position = cache length + depth,
+    int64 ([Build] "The Thinking Process Visible in Reasoning").
+
+    Returns (mask uint32 [B,N,W] with bit k of word k//32 set when node k is
+    visible to node i, depth int32 [B,N], positions int64 [B,N],
+    tree_ok int32 [B]).  An invalid tree gives mask 0, depth -1,
+    position -1 and tree_ok 0 for that request.
+    """
+    parents = np.asarray(parents)
+    B, N = parents.shape
+    W = (N + 31) // 32
+    if prefix_lens is None:
+        prefix_lens = np.zeros(B, dtype=np.int64)
+    mask = np.zeros((B, N, W), dtype=np.uint32)
+    depth = np.full((B, N), -1, dtype=np.int32)
+    positions = np.full((B, N), -1, dtype=np.int64)
+    ok = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        if not tree_is_valid(parents[b]):
+            continue
+        ok[b] = 1
+        for i in range(N):
+            k = i
+            steps = 0
+            while k != -1:
+                mask[b, i, k // 32] |= np.uint32(1 << (k % 32))
+                k = int(parents[b, k])
+                steps += 1
+            depth[b, i] = steps - 1
+            positions[b, i] = int(prefix_lens[b]) + steps - 1
+    return mask, depth, positions, ok
+
+
+def visible_nodes(mask_row: np.ndarray, n: int) -> list:
+    """Tree node indices whose bit is set in one node's mask words, ascending."""
+    return [k for k in range(n) if (int(mask_row[k // 32]) >> (k % 32)) & 1]
+
+
+# ----------------------------------------------------------------------------
+# Tree-verify attention, absorbed MLA form
+# ----------------------------------------------------------------------------
+
+def verify_attn_ref(q_lat, q_rope, ckv, krope, prefix_offsets, ckv_tree, krope_tree, mask, scale):
+    """Attention of every tree node over the shared prefix plus its visible tree nodes.
+
+    For request b, node i and head h, the key set J is the cached prefix rows
+    prefix_offsets[b] .. prefix_offsets[b+1]-1 followed by the tree nodes k
+    visible to i (mask bit k).  With c_j the latent row and r_j the rotary key,
+        s_j = scale * (q_lat[b,i,h] . c_j + q_rope[b,i,h] . r_j)
+        o   = sum_j softmax(s)_j c_j            (the value is the latent row)
+        lse = ln sum_j exp(s_j)
+    ([Validating] "Input Knowledge Required" for the absorbed MLA form and the
+    tree mask; [Running] "Input Knowledge Required": verify attention with
+    visibility masking).  Softmax is taken directly: max, exp, sum, divide.
+
+    Arguments are float arrays (converted to float64 here):
+      q_lat [B,N,H,Dl], q_rope [B,N,H,Dr], ckv [T,Dl], krope [T,Dr],
+      prefix_offsets int [B+1], ckv_tree [B,N,Dl], krope_tree [B,N,Dr],
+      mask uint32 [B,N,W].
+    Returns o float64 [B,N,H,Dl], lse float64 [B,N,H].
+    """
+    q_lat = np.asarray(q_lat, dtype=np.float64)
+    q_rope = np.asarray(q_rope, dtype=np.float64)
+    B, N, H, Dl = q_lat.shape
+    o = np.zeros((B, N, H, Dl), dtype=np.float64)
+    lse = np.zeros((B, N, H), dtype=np.float64)
+    for b in range(B):
+        s0, s1 = int(prefix_offsets[b]), int(prefix_offsets[b + 1])
+        C_prefix = np.asarray(ckv[s0:s1], dtype=np.float64)
+        R_prefix = np.asarray(krope[s0:s1], dtype=np.float64)
+        for i in range(N):
+            vis = visible_nodes(mask[b, i], N)
+            C = np.concatenate([C_prefix, np.asarray(ckv_tree[b, vis], dtype=np.float64)], axis=0)
+            R = np.concatenate([R_prefix, np.asarray(krope_tree[b, vis], dtype=np.float64)], axis=0)
+            S = scale * (q_lat[b, i] @ C.T + q_rope[b, i] @ R.T)          # [H, |J|]
+            m = S.max(axis=1, keepdims=True)
+            P = np.exp(S - m)
+            l = P.sum(axis=1, keepdims=True)
+            o[b, i] = (P @ C) / l
+            lse[b, i] = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Greedy tree accept
+# ----------------------------------------------------------------------------
+
+def target_argmax_ref(logits) -> np.ndarray:
+    """The target's greedy choice per tree node: first index of the maximum logit."""
+    return np.argmax(np.asarray(logits), axis=-1).astype(np.int32)
+
+
+def greedy_accept_ref(logits, tokens, parents):
+    """Longest root path whose draft tokens match the target's greedy choices.
+
+    ([Validating] "Input Knowledge Required": tokens along the longest
+    matching path are accepted; [Running] "Input Knowledge Required": greedy
+    token acceptance and path selection; [Build] "The Output Knowledge
+    Created": the longest prefix matching the target's greedy choices.)
+
+    Brute force: every node defines one root->node path; the path is
+    accepted when each non-root node's draft token equals the argmax of its
+    parent's logits.  The longest accepted path wins (ties: smallest
+    terminal node).  Commit = draft tokens of the path after the root, then
+    the terminal node's argmax.
+
+    Returns (target_argmax int32 [B,N], accept_len int32 [B] (drafts
+    accepted), accept_nodes int32 [B,N] (root first, -1 padded),
+    commit_tokens int32 [B,N] (accept_len+1 entries, -1 padded)).
+    """
+    tokens = np.asarray(tokens)
+    parents = np.asarray(parents)
+    B, N = tokens.shape
+    tstar = target_argmax_ref(logits)
+    accept_len = np.zeros(B, dtype=np.int32)
+    accept_nodes = np.full((B, N), -1, dtype=np.int32)
+    commit = np.full((B, N), -1, dtype=np.int32)
+    for b in range(B):
+        if not tree_is_valid(parents[b]):
+            raise ValueError(f"request {b}: not a valid tree")
+        best = None
+        for t in range(N):
+            path = [t]
+            while int(parents[b, path[-1]]) != -1:
+                path.append(int(parents[b, path[-1]]))
+            path.reverse()                      # root ... t
+            if all(int(tokens[b, path[k]]) == int(tstar[b, path[k - 1]]) for k in range(1, len(path))):
+                if best is None or len(path) > len(best):
+                    best = path
+        accept_len[b] = len(best) - 1
+        accept_nodes[b, :len(best)] = best
+        committed = [int(tokens[b, k]) for k in best[1:]] + [int(tstar[b, best[-1]])]
+        commit[b, :len(committed)] = committed
+    return tstar, accept_len, accept_nodes, commit

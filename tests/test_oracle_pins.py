@@ -1,0 +1,486 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test fixes the oracle to a closed form, a special case that reduces to a
+library routine (torch's scaled_dot_product_attention / logsumexp in float64
+on the CPU), an algebraically different formulation (the unabsorbed MLA form,
+the dense -inf mask form, the per-path causal form, the split/merge identity)
+or brute force on tiny inputs.  A dropped term, a wrong sign or index or a
+transposed operand anywhere in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import build_mask_ref, greedy_accept_ref, target_argmax_ref, verify_attn_ref
+from synth import bounded_tree, chain_tree, make_config, make_workload, uniform_tree
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# helpers that are independent of the oracle's code
+# ----------------------------------------------------------------------------
+
+def closure_visibility(parent_row):
+    """Ancestor-or-self relation as a dense bool matrix, by boolean matrix powers."""
+    n = len(parent_row)
+    A = np.zeros((n, n), dtype=bool)
+    for i in range(1, n):
+        A[i, parent_row[i]] = True
+    R = np.eye(n, dtype=bool)
+    step = A.copy()
+    for _ in range(n):
+        R |= step
+        step = (step.astype(np.int64) @ A.astype(np.int64)) > 0
+    return R
+
+
+def pack_words(vis):
+    """Dense bool [N, N] -> uint32 words [N, W], bit k%32 of word k//32."""
+    n = vis.shape[0]
+    w = (n + 31) // 32
+    padded = np.zeros((n, 32 * w), dtype=bool)
+    padded[:, :n] = vis
+    by = np.packbits(padded, axis=1, bitorder="little")
+    return by.view(np.uint32).reshape(n, w) if by.shape[1] % 4 == 0 else None
+
+
+def sdpa(q, k, v, mask, scale):
+    """torch scaled_dot_product_attention in float64. q [H,nq,d], k/v [nk,*], mask bool [nq,nk]."""
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64))
+    kt = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float64)).unsqueeze(0).expand(qt.shape[0], -1, -1)
+    vt = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64)).unsqueeze(0).expand(qt.shape[0], -1, -1)
+    m = None if mask is None else torch.from_numpy(mask)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    return out.numpy()
+
+
+def torch_lse(scores, mask):
+    s = torch.from_numpy(np.ascontiguousarray(scores, dtype=np.float64))
+    if mask is not None:
+        s = s.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    return torch.logsumexp(s, dim=-1).numpy()
+
+
+def f64_case(w):
+    q = w.f32("q_lat").astype(np.float64)
+    qr = w.f32("q_rope").astype(np.float64)
+    kv = w.f32("kv").astype(np.float64)
+    kt = w.f32("kv_tree").astype(np.float64)
+    return q, qr, kv[:, :w.Dl], kv[:, w.Dl:], kt[..., :w.Dl], kt[..., w.Dl:]
+
+
+def run_oracle(w):
+    mask, depth, pos, ok = build_mask_ref(w.parents, w.prefix_lens)
+    q, qr, c, r, ct, rt = f64_case(w)
+    o, lse = verify_attn_ref(q, qr, c, r, w.prefix_offsets, ct, rt, mask, w.scale)
+    return mask, depth, o, lse
+
+
+def small(seed, B=2, N=12, H=3, Dl=16, Dr=8, L=(5, 9), tree=("uniform",), std=1.0):
+    return make_workload(B=B, N=N, H=H, Dl=Dl, Dr=Dr, dtype="f32", std=std, scale=0.37,
+                         prefix=("list", list(L)), tree=tree, seed=seed)
+
+
+# ----------------------------------------------------------------------------
+# visibility mask, depth, positions
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("n", [1, 2, 7, 32, 33, 64, 100])
+def test_mask_equals_transitive_closure(seed, n):
+    rng = np.random.default_rng(seed)
+    trees = [chain_tree(n), uniform_tree(rng, n), np.array([-1] + [0] * (n - 1), np.int32)]
+    if n > 1:
+        trees.append(bounded_tree(rng, n, 12, 4))
+    parents = np.stack(trees)
+    lens = rng.integers(0, 1000, size=len(trees))
+    mask, depth, pos, ok = build_mask_ref(parents, lens)
+    assert ok.tolist() == [1] * len(trees)
+    assert mask.shape == (len(trees), n, (n + 31) // 32)
+    for b in range(len(trees)):
+        vis = closure_visibility(parents[b])
+        packed = pack_words(vis)
+        assert np.array_equal(mask[b], packed)
+        # ancestor-or-self set size is depth + 1
+        assert np.array_equal(vis.sum(axis=1) - 1, depth[b])
+        assert np.array_equal(pos[b], lens[b] + depth[b].astype(np.int64))
+
+
+def test_depth_special_trees():
+    mask, depth, pos, ok = build_mask_ref(np.stack([chain_tree(9), np.array([-1] + [0] * 8, np.int32)]))
+    assert depth[0].tolist() == list(range(9))
+    assert depth[1].tolist() == [0] + [1] * 8
+    assert pos.tolist() == depth.tolist()      # no prefix lengths: position = depth
+    # star: every node sees the root and itself only
+    assert all(int(mask[1, i, 0]) == (1 | (1 << i)) for i in range(9))
+
+
+def test_mask_bit_layout_crosses_words():
+    n = 40
+    mask, depth, _, _ = build_mask_ref(chain_tree(n)[None])
+    assert int(mask[0, 39, 0]) == 0xFFFFFFFF and int(mask[0, 39, 1]) == 0xFF
+    assert int(mask[0, 32, 1]) == 1 and int(mask[0, 31, 1]) == 0
+
+
+@pytest.mark.parametrize("bad", [
+    [0, 0, 1],        # root parent not -1
+    [-1, 1, 0],       # self parent
+    [-1, 0, 3, 0],    # forward parent
+    [-1, -1, 0],      # second root
+    [-1, 0, -5],      # negative parent
+])
+def test_invalid_tree_flagged(bad):
+    parents = np.stack([np.array(bad, np.int32), chain_tree(len(bad))])
+    mask, depth, pos, ok = build_mask_ref(parents, np.array([3, 4]))
+    assert ok.tolist() == [0, 1]
+    assert not mask[0].any() and (depth[0] == -1).all() and (pos[0] == -1).all()
+    assert depth[1].tolist() == list(range(len(bad)))
+
+
+# ----------------------------------------------------------------------------
+# attention: absorbed MLA form against the unabsorbed form (torch SDPA)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_absorbed_equals_unabsorbed(seed):
+    """o_lat mapped through W_UV equals explicit attention with K = [W_UK c ; r], V = W_UV c."""
+    H, Dl, Dr, Dn, Dv = 3, 16, 8, 6, 5
+    w = small(seed, H=H, Dl=Dl, Dr=Dr, tree=("bounded", 4, 3))
+    rng = np.random.default_rng(100 + seed)
+    W_UK = rng.standard_normal((H, Dn, Dl))       # k_nope = W_UK c
+    W_UV = rng.standard_normal((H, Dv, Dl))       # v = W_UV c
+    _, qr, c, r, ct, rt = f64_case(w)
+    q_nope = rng.standard_normal((w.B, w.N, H, Dn))
+    q_lat = np.einsum("bnhd,hdl->bnhl", q_nope, W_UK)   # absorbed query: W_UK^T q_nope
+    mask, _, _, _ = build_mask_ref(w.parents, w.prefix_lens)
+    o_lat, lse = verify_attn_ref(q_lat, qr, c, r, w.prefix_offsets, ct, rt, mask, w.scale)
+    for b in range(w.B):
+        s0, s1 = int(w.prefix_offsets[b]), int(w.prefix_offsets[b + 1])
+        L = s1 - s0
+        vis = closure_visibility(w.parents[b])
+        allowed = np.concatenate([np.ones((w.N, L), bool), vis], axis=1)       # [N, L+N]
+        C = np.concatenate([c[s0:s1], ct[b]])
+        R = np.concatenate([r[s0:s1], rt[b]])
+        for h in range(H):
+            K = np.concatenate([C @ W_UK[h].T, R], axis=1)                     # [L+N, Dn+Dr]
+            Vv = C @ W_UV[h].T                                                  # [L+N, Dv]
+            Q = np.concatenate([q_nope[b, :, h], qr[b, :, h]], axis=1)          # [N, Dn+Dr]
+            ref = sdpa(Q[None], K, Vv, allowed, w.scale)[0]
+            got = o_lat[b, :, h] @ W_UV[h].T
+            np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+            ref_lse = torch_lse(w.scale * (Q @ K.T), allowed)
+            np.testing.assert_allclose(lse[b, :, h], ref_lse, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_general_tree_matches_sdpa_latent(seed):
+    """Library cross-check in the latent space with an explicit boolean mask."""
+    w = small(seed, B=3, N=20, L=(0, 3, 17), tree=("uniform",))
+    mask, depth, o, lse = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    for b in range(w.B):
+        s0, s1 = int(w.prefix_offsets[b]), int(w.prefix_offsets[b + 1])
+        allowed = np.concatenate([np.ones((w.N, s1 - s0), bool), closure_visibility(w.parents[b])], axis=1)
+        K = np.concatenate([np.concatenate([c[s0:s1], ct[b]]), np.concatenate([r[s0:s1], rt[b]])], axis=1)
+        V = np.concatenate([c[s0:s1], ct[b]])
+        Q = np.concatenate([q[b], qr[b]], axis=2).transpose(1, 0, 2)            # [H, N, Dl+Dr]
+        ref = sdpa(Q, K, V, allowed, w.scale).transpose(1, 0, 2)
+        np.testing.assert_allclose(o[b], ref, rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# special trees that reduce to textbook attention
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L", [0, 1, 8, 50])
+def test_chain_equals_causal(L):
+    """A single chain verifies exactly like causal attention over prefix ++ chain."""
+    w = make_workload(B=1, N=9, H=4, Dl=32, Dr=16, dtype="f32", std=1.0, scale=0.21,
+                      prefix=("fixed", L), tree=("chain",), seed=L)
+    _, _, o, lse = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    K = np.concatenate([np.concatenate([c, ct[0]]), np.concatenate([r, rt[0]])], axis=1)
+    V = np.concatenate([c, ct[0]])
+    Q = np.concatenate([q[0], qr[0]], axis=2).transpose(1, 0, 2)
+    # causal with the queries at the last N positions (bottom-right aligned)
+    n, T = w.N, L + w.N
+    allowed = np.arange(T)[None, :] <= (L + np.arange(n))[:, None]
+    ref = sdpa(Q, K, V, allowed, w.scale).transpose(1, 0, 2)
+    np.testing.assert_allclose(o[0], ref, rtol=1e-11, atol=1e-12)
+    # full square causal through torch's own causal flag: last N rows of a causal pass
+    keys_as_queries = np.zeros((w.H, T, Q.shape[2]))
+    keys_as_queries[:, L:] = Q
+    qt = torch.from_numpy(keys_as_queries)
+    kt = torch.from_numpy(K).unsqueeze(0).expand(w.H, -1, -1)
+    vt = torch.from_numpy(V).unsqueeze(0).expand(w.H, -1, -1)
+    full = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=w.scale).numpy()
+    np.testing.assert_allclose(o[0], full[:, L:].transpose(1, 0, 2), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("L", [0, 5, 300])
+def test_single_node_equals_decode(L):
+    """N = 1: the root alone is plain decode attention over L + 1 keys."""
+    w = make_workload(B=1, N=1, H=5, Dl=24, Dr=8, dtype="f32", std=1.0, scale=0.3,
+                      prefix=("fixed", L), tree=("chain",), seed=7 + L)
+    _, _, o, lse = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    K = np.concatenate([np.concatenate([c, ct[0]]), np.concatenate([r, rt[0]])], axis=1)
+    V = np.concatenate([c, ct[0]])
+    Q = np.concatenate([q[0, 0], qr[0, 0]], axis=1)[:, None, :]               # [H, 1, d]
+    ref = sdpa(Q, K, V, None, w.scale)[:, 0]
+    np.testing.assert_allclose(o[0, 0], ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], torch_lse(w.scale * (Q[:, 0] @ K.T), None), rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_each_node_equals_causal_over_its_path(seed):
+    """Node i's output is the last row of causal attention over prefix ++ path(root -> i)."""
+    w = small(seed, B=1, N=16, L=(11,), tree=("bounded", 5, 3))
+    _, depth, o, lse = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    for i in range(w.N):
+        path = [i]
+        while w.parents[0, path[-1]] != -1:
+            path.append(int(w.parents[0, path[-1]]))
+        path = path[::-1]
+        K = np.concatenate([np.concatenate([c, ct[0, path]]), np.concatenate([r, rt[0, path]])], axis=1)
+        V = np.concatenate([c, ct[0, path]])
+        Q = np.concatenate([q[0, i], qr[0, i]], axis=1)[:, None, :]
+        ref = sdpa(Q, K, V, None, w.scale)[:, 0]
+        np.testing.assert_allclose(o[0, i], ref, rtol=1e-11, atol=1e-12)
+        assert len(path) == depth[0, i] + 1
+
+
+def test_dense_minus_inf_mask_form():
+    """Scores over all L+N keys with -inf on invisible tree keys give the same result."""
+    w = small(3, B=2, N=24, L=(7, 13), tree=("uniform",))
+    mask, _, o, lse = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    for b in range(w.B):
+        s0, s1 = int(w.prefix_offsets[b]), int(w.prefix_offsets[b + 1])
+        C = np.concatenate([c[s0:s1], ct[b]])
+        R = np.concatenate([r[s0:s1], rt[b]])
+        vis = closure_visibility(w.parents[b])
+        for h in range(w.H):
+            S = w.scale * (q[b, :, h] @ C.T + qr[b, :, h] @ R.T)
+            S[:, s1 - s0:][~vis] = -np.inf
+            P = torch.softmax(torch.from_numpy(S), dim=1).numpy()
+            np.testing.assert_allclose(o[b, :, h], P @ C, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(lse[b, :, h], torch.logsumexp(torch.from_numpy(S), 1).numpy(), rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+
+def test_zero_query_closed_form():
+    """q = 0: uniform weights, lse = ln(L + depth + 1), o = mean of the visible latent rows."""
+    w = small(5, B=2, N=10, L=(4, 0), tree=("uniform",))
+    mask, depth, _, _ = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    o, lse = verify_attn_ref(np.zeros_like(q), np.zeros_like(qr), c, r, w.prefix_offsets, ct, rt, mask, w.scale)
+    for b in range(w.B):
+        s0, s1 = int(w.prefix_offsets[b]), int(w.prefix_offsets[b + 1])
+        vis = closure_visibility(w.parents[b])
+        for i in range(w.N):
+            n_keys = (s1 - s0) + depth[b, i] + 1
+            np.testing.assert_allclose(lse[b, i], math.log(n_keys), rtol=0, atol=1e-14)
+            rows = np.concatenate([c[s0:s1], ct[b, vis[i]]])
+            np.testing.assert_allclose(o[b, i], np.broadcast_to(rows.mean(axis=0), o[b, i].shape), atol=1e-14)
+
+
+def test_constant_value_rows_give_that_row():
+    w = small(6, B=1, N=9, L=(20,))
+    mask, _, _, _ = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    v = np.linspace(-2, 3, w.Dl)
+    c2 = np.broadcast_to(v, c.shape).copy()
+    ct2 = np.broadcast_to(v, ct.shape).copy()
+    # scores then depend on r only; the output must still be v exactly (up to rounding)
+    o, _ = verify_attn_ref(q, qr, c2, r, w.prefix_offsets, ct2, rt, mask, w.scale)
+    np.testing.assert_allclose(o, np.broadcast_to(v, o.shape), rtol=0, atol=1e-13)
+
+
+def test_dominant_key_selects_its_row():
+    """One key with a score far above the rest: o is that key's latent row, lse its score."""
+    w = small(7, B=1, N=6, L=(15,), tree=("chain",))
+    mask, _, _, _ = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    r = r * 0.0
+    rt = rt * 0.0
+    qr = np.ones_like(qr)
+    j = 9
+    r[j] = 1000.0 / (w.scale * w.Dr)              # rope score of key j = 1000
+    o, lse = verify_attn_ref(np.zeros_like(q), qr, c, r, w.prefix_offsets, ct, rt, mask, w.scale)
+    np.testing.assert_allclose(o, np.broadcast_to(c[j], o.shape), atol=1e-12)
+    np.testing.assert_allclose(lse, 1000.0, atol=1e-9)
+
+
+def test_prefix_row_order_is_irrelevant():
+    w = small(8, B=1, N=7, L=(30,))
+    mask, _, o, lse = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    perm = np.random.default_rng(0).permutation(30)
+    o2, lse2 = verify_attn_ref(q, qr, c[perm], r[perm], w.prefix_offsets, ct, rt, mask, w.scale)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13)
+
+
+@pytest.mark.parametrize("cut", [0, 1, 13, 29, 30])
+def test_split_merge_identity(cut):
+    """Partials over a partition of the keys merge by the log-sum-exp weights to the whole."""
+    w = small(9, B=1, N=11, L=(30,), tree=("uniform",))
+    mask, _, o, lse = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    no_tree = np.zeros_like(mask)
+    # part 1: prefix rows [0, cut) and no tree nodes; part 2: rows [cut, L) and the tree
+    o2, l2 = verify_attn_ref(q, qr, c[cut:], r[cut:], np.array([0, 30 - cut]), ct, rt, mask, w.scale)
+    if cut == 0:                  # part 1 is empty: part 2 is the whole key set
+        np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-13)
+        return
+    o1, l1 = verify_attn_ref(q, qr, c[:cut], r[:cut], np.array([0, cut]), ct, rt, no_tree, w.scale)
+    lm = np.logaddexp(l1, l2)
+    om = np.exp(l1 - lm)[..., None] * o1 + np.exp(l2 - lm)[..., None] * o2
+    np.testing.assert_allclose(lm, lse, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(om, o, rtol=1e-11, atol=1e-13)
+
+
+def test_scale_zero_is_uniform():
+    w = small(10, B=1, N=5, L=(6,))
+    mask, depth, _, _ = run_oracle(w)
+    q, qr, c, r, ct, rt = f64_case(w)
+    o0, l0 = verify_attn_ref(q, qr, c, r, w.prefix_offsets, ct, rt, mask, 0.0)
+    oz, lz = verify_attn_ref(0 * q, 0 * qr, c, r, w.prefix_offsets, ct, rt, mask, w.scale)
+    np.testing.assert_allclose(o0, oz, atol=1e-14)
+    np.testing.assert_allclose(l0, lz, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# greedy accept
+# ----------------------------------------------------------------------------
+
+def accept_by_propagation(tstar, tokens, parents):
+    """O(N) form: valid[i] = valid[parent] and token matches; deepest valid node, smallest index."""
+    B, N = tokens.shape
+    out = []
+    for b in range(B):
+        valid = np.zeros(N, bool)
+        d = np.zeros(N, int)
+        valid[0] = True
+        for i in range(1, N):
+            p = parents[b, i]
+            d[i] = d[p] + 1
+            valid[i] = valid[p] and tokens[b, i] == tstar[b, p]
+        cand = np.nonzero(valid)[0]
+        term = int(cand[np.argmax(d[cand])])          # first maximum -> smallest index
+        path = [term]
+        while parents[b, path[-1]] != -1:
+            path.append(int(parents[b, path[-1]]))
+        out.append((d[term], path[::-1]))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("p_match", [0.0, 0.5, 0.9, 1.0])
+def test_accept_brute_force_equals_propagation(seed, p_match):
+    w = make_workload(B=3, N=24, H=1, Dl=1, Dr=1, dtype="f32", std=1.0, scale=1.0, prefix=("fixed", 0),
+                      tree=("uniform",) if seed % 2 else ("bounded", 6, 3), V=50, p_match=p_match, seed=seed)
+    tstar, alen, nodes, commit = greedy_accept_ref(w.logits, w.tokens, w.parents)
+    for b, (d, path) in enumerate(accept_by_propagation(tstar, w.tokens, w.parents)):
+        assert alen[b] == d
+        assert nodes[b, :d + 1].tolist() == path and (nodes[b, d + 1:] == -1).all()
+        assert commit[b, :d].tolist() == [int(w.tokens[b, k]) for k in path[1:]]
+        assert commit[b, d] == tstar[b, path[-1]] and (commit[b, d + 1:] == -1).all()
+
+
+def test_planted_winner_is_the_argmax():
+    w = make_config(2)
+    assert np.array_equal(target_argmax_ref(w.logits), w.winners)
+
+
+def test_chain_fully_matched_commits_block():
+    w = make_config(1)
+    tstar, alen, nodes, commit = greedy_accept_ref(w.logits, w.tokens, w.parents)
+    assert alen.tolist() == [7]
+    assert nodes[0].tolist() == list(range(8))
+    assert commit[0].tolist() == [int(t) for t in w.tokens[0, 1:]] + [int(tstar[0, 7])]
+
+
+def test_pages_chain8_golden():
+    """Block size 8 with a drafter that always proposes the target's choice: 8 tokens per
+    verify step, 24 tokens in 3 steps (golden values printed on the pages)."""
+    with open(os.path.join(GOLDEN, "pages_chain8_block.json")) as f:
+        g = json.load(f)
+    committed = 0
+    steps = 0
+    for step in range(g["verify_steps"]):
+        w = make_workload(B=1, N=g["block_size"], H=1, Dl=1, Dr=1, dtype="f32", std=1.0, scale=1.0,
+                          prefix=("fixed", 0), tree=("chain",), V=g["vocab"], p_match=1.0, seed=1000 + step)
+        _, alen, _, commit = greedy_accept_ref(w.logits, w.tokens, w.parents)
+        committed += int((commit[0] >= 0).sum())
+        steps += 1
+        assert alen[0] + 1 == g["tokens_per_verify_step"]
+    assert committed == g["tokens_generated"] and steps == g["verify_steps"]
+
+
+def test_accept_single_node_is_greedy_decode():
+    logits = np.array([[[0.1, 3.0, -1.0, 2.9]]], np.float32)
+    tstar, alen, nodes, commit = greedy_accept_ref(logits, np.array([[2]]), np.array([[-1]]))
+    assert alen.tolist() == [0] and nodes.tolist() == [[0]] and commit.tolist() == [[1]]
+
+
+def test_accept_all_mismatched():
+    w = make_workload(B=2, N=10, H=1, Dl=1, Dr=1, dtype="f32", std=1.0, scale=1.0, prefix=("fixed", 0),
+                      tree=("uniform",), V=40, p_match=0.0, seed=3)
+    tstar, alen, nodes, commit = greedy_accept_ref(w.logits, w.tokens, w.parents)
+    assert alen.tolist() == [0, 0]
+    assert (nodes[:, 0] == 0).all() and (nodes[:, 1:] == -1).all()
+    assert commit[:, 0].tolist() == tstar[:, 0].tolist() and (commit[:, 1:] == -1).all()
+
+
+def test_argmax_ties_pick_lowest_index():
+    logits = np.zeros((1, 3, 6), np.float32)
+    logits[0, 0, [2, 4]] = 5.0
+    logits[0, 1, :] = -np.inf
+    logits[0, 2, [5, 1, 3]] = [1.0, 1.0, 1.0]
+    assert target_argmax_ref(logits).tolist() == [[2, 0, 1]]
+
+
+def test_duplicate_matching_siblings_longest_then_smallest():
+    #        0
+    #      / | \
+    #     1  2  3          tokens of 1, 2, 3 all equal argmax(0) = 7
+    #     |  |  |
+    #     4  5  6          4 and 6 match their parents; 5 does not
+    #        |
+    #        7             (child of 5, matches, but 5 is rejected)
+    parents = np.array([[-1, 0, 0, 0, 1, 2, 3, 5]], np.int32)
+    V = 10
+    logits = np.zeros((1, 8, V), np.float32)
+    am = [7, 2, 3, 4, 9, 6, 8, 1]
+    for i, a in enumerate(am):
+        logits[0, i, a] = 1.0
+    tokens = np.array([[0, 7, 7, 7, 2, 0, 4, 6]], np.int32)
+    tstar, alen, nodes, commit = greedy_accept_ref(logits, tokens, parents)
+    assert tstar[0].tolist() == am
+    assert alen.tolist() == [2]
+    assert nodes[0].tolist() == [0, 1, 4, -1, -1, -1, -1, -1]    # 0-1-4 and 0-3-6 tie: smallest terminal
+    assert commit[0].tolist() == [7, 2, 9, -1, -1, -1, -1, -1]
+
+
+def test_longer_branch_beats_earlier_sibling():
+    # 0 -> 1 (match, leaf); 0 -> 2 (match) -> 3 (match): the longer path through 2 wins
+    parents = np.array([[-1, 0, 0, 2]], np.int32)
+    logits = np.zeros((1, 4, 5), np.float32)
+    for i, a in enumerate([3, 0, 1, 2]):
+        logits[0, i, a] = 1.0
+    tokens = np.array([[4, 3, 3, 1]], np.int32)
+    _, alen, nodes, commit = greedy_accept_ref(logits, tokens, parents)
+    assert alen.tolist() == [2]
+    assert nodes[0].tolist() == [0, 2, 3, -1]
+    assert commit[0].tolist() == [3, 1, 2, -1]
