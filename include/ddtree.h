@@ -1,0 +1,173 @@
+/*
+ * ddtree.h -- C ABI of the MI355X (gfx950) DDTree tree-verify library.
+ *
+ * The library implements the data-parallel hot path of verifying a draft
+ * tree in one target forward: the visibility mask built from a parent array,
+ * the tree-verify MLA attention in absorbed form over the shared latent KV
+ * cache prefix plus each node's own ancestors, and the greedy tree accept.
+ *
+ * Pages cited (titles of the source pages):
+ *   [Validating] "The Moment of Proof: Validating a Native CUDA Speculative Decoding Engine"
+ *   [Running]    "The Moment of Proof: Running the Native DDTree Speculative Decoding Engine"
+ *   [Build]      "The Build That Proved It: Compiling the Native DDTree Speculative Decoding Engine"
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" are HIP device memory owned by the caller; the
+ *     library allocates nothing, keeps no state between calls and is safe to
+ *     call from several host threads.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns; nothing synchronises.
+ *   - Arrays are dense row-major (C order) unless a leading dimension (ld_*,
+ *     in elements) is given for their rows.
+ *   - The return value is a ddtree_status.  Arguments are validated on the
+ *     host before anything is enqueued; an invalid call enqueues nothing.
+ *     DDTREE_ERR_HIP reports a failed launch (hipGetLastError).  Problems that
+ *     depend on device data (a malformed tree) are reported on the device
+ *     through tree_ok.
+ *   - Outputs must not overlap inputs or each other (checked where the
+ *     extents are known on the host).
+ *   - Tree layout: node 0 is the root (the last committed token), parent[0] =
+ *     -1 and 0 <= parent[i] < i for i >= 1; at most DDTREE_MAX_NODES nodes.
+ */
+#ifndef DDTREE_H
+#define DDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDTREE_MAX_NODES 256
+
+typedef enum {
+  DDTREE_OK = 0,
+  DDTREE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment or overlapping buffers */
+  DDTREE_ERR_UNSUPPORTED = -2, /* shape or dtype outside what the kernels implement */
+  DDTREE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than ddtree_verify_attn_workspace_size */
+  DDTREE_ERR_HIP = -4          /* the HIP runtime reported an error for a launch */
+} ddtree_status;
+
+typedef enum {
+  DDTREE_F32 = 0,  /* float32 inputs, float32 arithmetic */
+  DDTREE_BF16 = 1  /* bfloat16 inputs, bf16 MFMA products with float32 accumulation */
+} ddtree_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* ddtree_status_string(int status);
+
+/*
+ * ddtree_build_mask -- ancestor-or-self visibility mask, depth and positions.
+ *
+ * Defines the custom attention mask under which a draft tree is verified in
+ * one forward ([Validating] "Input Knowledge Required"; attention mask
+ * construction in the decode loop: [Validating] "Output Knowledge Created"),
+ * and positions = cache length + node depth as int64 ([Build] "The Thinking
+ * Process Visible in Reasoning").
+ *
+ *   parents        device int32 [B, N]       parent array per request
+ *   B, N           requests (>= 0) and nodes per request (1 .. DDTREE_MAX_NODES)
+ *   prefix_offsets device int64 [B + 1] or NULL; L_b = offsets[b+1] - offsets[b]
+ *                  (NULL: L_b = 0)
+ *   mask           device uint32 [B, N, W], W = ceil(N / 32): bit k % 32 of word
+ *                  k / 32 of row (b, i) is set iff node k is node i or one of
+ *                  its ancestors
+ *   depth          device int32 [B, N]       parent steps from node i to the root
+ *   positions      device int64 [B, N] or NULL: L_b + depth
+ *   tree_ok        device int32 [B]          1 if request b's parent array is a
+ *                  valid tree, else 0; then its mask row words are 0 and its
+ *                  depth and positions are -1
+ */
+int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_t* prefix_offsets,
+                      uint32_t* mask, int32_t* depth, int64_t* positions, int32_t* tree_ok, void* stream);
+
+/*
+ * ddtree_verify_attn -- tree-verify attention, MLA absorbed form.
+ *
+ * Every tree node's absorbed query attends to its request's cached latent
+ * prefix plus the tree nodes its mask row makes visible ([Validating] "Input
+ * Knowledge Required": the absorb form folds the key/value up-projections
+ * into attention, and the draft tree is verified under a custom mask;
+ * [Running] "Input Knowledge Required": verify attention with visibility
+ * masking).  For request b, node i, head h and visible key j with latent row
+ * c_j (Dl wide) and rotary key r_j (Dr wide, already rotated):
+ *     s_j = softmax_scale * (q_lat[b,i,h] . c_j + q_rope[b,i,h] . r_j)
+ *     o[b,i,h]   = sum_j softmax(s)_j * c_j   (latent output; the caller applies
+ *                                              the value up-projection)
+ *     lse[b,i,h] = ln sum_j exp(s_j)
+ *
+ *   dtype            DDTREE_BF16: (Dl, Dr) = (512, 64) on the MFMA kernel;
+ *                    DDTREE_F32: any Dl in 1..512, Dr in 0..512
+ *   B, N, H          requests, nodes per request (<= DDTREE_MAX_NODES), heads
+ *   q_lat            device [B, N, H, Dl], dense
+ *   q_rope           device [B, N, H, Dr], dense
+ *   ckv, ld_ckv      device packed prefix latent rows: row t at ckv + t*ld_ckv
+ *   krope, ld_krope  device packed prefix rotary keys: row t at krope + t*ld_krope
+ *                    (the usual fused cache [T, Dl+Dr] is krope = ckv + Dl, both
+ *                    ld = Dl + Dr)
+ *   prefix_offsets   device int64 [B + 1]: request b owns rows offsets[b] ..
+ *                    offsets[b+1]-1 (lengths may be 0)
+ *   max_prefix_len   host value >= every L_b; only used to plan the KV split
+ *   ckv_tree, ld_ckv_tree      device tree-node latent rows: node (b,i) at
+ *                              ckv_tree + (b*N + i)*ld_ckv_tree
+ *   krope_tree, ld_krope_tree  device tree-node rotary keys, same indexing
+ *   mask             device uint32 [B, N, ceil(N/32)] from ddtree_build_mask
+ *   softmax_scale    finite scale applied to q.k (e.g. 1/sqrt(qk head dim))
+ *   num_splits       number of KV splits per query block, 0 = automatic
+ *   o                device float32 [B, N, H, Dl]
+ *   lse              device float32 [B, N, H] (natural log)
+ *   workspace        device scratch of workspace_bytes >=
+ *                    ddtree_verify_attn_workspace_size(...) with the same shape
+ *                    and num_splits (may be NULL when that size is 0)
+ * bf16 inputs need 16-byte aligned base pointers and row strides that are
+ * multiples of 8 elements.  Requests whose tree_ok is 0 give undefined o/lse.
+ */
+size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
+                                         int64_t max_prefix_len, int32_t num_splits);
+
+/* The KV split count that num_splits = 0 selects for this shape (>= 1). */
+int32_t ddtree_verify_attn_auto_splits(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
+                                       int64_t max_prefix_len);
+
+int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
+                       const void* q_lat, const void* q_rope,
+                       const void* ckv, int64_t ld_ckv, const void* krope, int64_t ld_krope,
+                       const int64_t* prefix_offsets, int64_t max_prefix_len,
+                       const void* ckv_tree, int64_t ld_ckv_tree, const void* krope_tree, int64_t ld_krope_tree,
+                       const uint32_t* mask, float softmax_scale, int32_t num_splits,
+                       float* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ddtree_greedy_accept -- target argmax per node and the accepted path.
+ *
+ * The tokens along the longest root path whose draft tokens match the
+ * target's greedy choices are accepted ([Validating] "Input Knowledge
+ * Required"; [Running] "Input Knowledge Required": greedy token acceptance
+ * and path selection; [Build] "The Output Knowledge Created": the longest
+ * prefix matching the target's greedy choices).  Node i (i >= 1) is accepted
+ * when its parent is accepted and tokens[b,i] == target_argmax[b,parent[i]];
+ * the root is always accepted.  The accepted node of greatest depth is the
+ * terminal (ties: smallest index).  Commit = the draft tokens of the path
+ * after the root, then target_argmax of the terminal (the bonus token).
+ *
+ *   logits, ld_logits  device float32 rows [B*N] of V logits, row (b,i) at
+ *                      logits + (b*N + i)*ld_logits (ld_logits >= V)
+ *   tokens             device int32 [B, N] draft token per node (root unused)
+ *   parents            device int32 [B, N] valid trees (ddtree_build_mask's tree_ok)
+ *   B, N, V            requests, nodes (1 .. DDTREE_MAX_NODES), vocabulary (>= 1)
+ *   target_argmax      device int32 [B, N]: first index of each row's maximum
+ *                      (NaN logits are not supported)
+ *   accept_len         device int32 [B]: accepted draft tokens (terminal depth)
+ *   accept_nodes       device int32 [B, N]: path root..terminal, then -1
+ *   commit_tokens      device int32 [B, N]: accept_len + 1 tokens, then -1
+ */
+int ddtree_greedy_accept(const float* logits, int64_t ld_logits, const int32_t* tokens, const int32_t* parents,
+                         int32_t B, int32_t N, int32_t V, int32_t* target_argmax, int32_t* accept_len,
+                         int32_t* accept_nodes, int32_t* commit_tokens, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDTREE_H */

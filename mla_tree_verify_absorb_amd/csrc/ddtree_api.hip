@@ -1,0 +1,223 @@
+// C ABI entry points: host-side argument validation, KV split planning and
+// kernel launches.  Every check runs before the first HIP call, so an invalid
+// call enqueues nothing (and can be tested on a machine without a GPU).
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/ddtree.h"
+#include "ddtree_internal.h"
+
+using namespace ddtree;
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range range_of(const void* p, uint64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+bool overlaps(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool bf16_shape_supported(int Dl, int Dr) { return Dl == kMfmaDl && Dr == kMfmaDr; }
+
+// KV splits per query block: enough workgroups to cover the 256 CUs once,
+// while every split keeps at least 4 KV tiles (128 keys).
+int auto_splits(int dtype, int B, int N, int H, int64_t max_prefix_len) {
+  if (dtype != DDTREE_BF16 || B <= 0 || N <= 0 || H <= 0) return 1;
+  const int64_t n_rb = ceil_div((int64_t)N * H, kRowsPerBlock);
+  const int64_t wg = (int64_t)B * n_rb;
+  int64_t s = wg >= 256 ? 1 : ceil_div(256, wg);
+  const int64_t max_tiles = ceil_div(max_prefix_len > 0 ? max_prefix_len : 0, kKeysPerTile) + ceil_div(N, kKeysPerTile);
+  const int64_t cap = max_tiles / 4 > 1 ? max_tiles / 4 : 1;
+  if (s > cap) s = cap;
+  if (s > 64) s = 64;
+  return (int)(s < 1 ? 1 : s);
+}
+
+int resolve_splits(int dtype, int B, int N, int H, int64_t max_prefix_len, int num_splits) {
+  if (dtype != DDTREE_BF16) return 1;
+  return num_splits > 0 ? num_splits : auto_splits(dtype, B, N, H, max_prefix_len);
+}
+
+size_t workspace_bytes_for(int dtype, int B, int N, int H, int Dl, int splits) {
+  if (dtype != DDTREE_BF16 || splits <= 1) return 0;
+  const uint64_t rows = (uint64_t)B * N * H;
+  return (size_t)(splits * rows * (uint64_t)(Dl + 1) * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ddtree_status_string(int status) {
+  switch (status) {
+    case DDTREE_OK: return "DDTREE_OK";
+    case DDTREE_ERR_INVALID_ARG: return "DDTREE_ERR_INVALID_ARG";
+    case DDTREE_ERR_UNSUPPORTED: return "DDTREE_ERR_UNSUPPORTED";
+    case DDTREE_ERR_WORKSPACE: return "DDTREE_ERR_WORKSPACE";
+    case DDTREE_ERR_HIP: return "DDTREE_ERR_HIP";
+    default: return "DDTREE_UNKNOWN_STATUS";
+  }
+}
+
+int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_t* prefix_offsets, uint32_t* mask,
+                      int32_t* depth, int64_t* positions, int32_t* tree_ok, void* stream) {
+  if (B < 0 || N < 1) return DDTREE_ERR_INVALID_ARG;
+  if (N > DDTREE_MAX_NODES) return DDTREE_ERR_UNSUPPORTED;
+  if (B == 0) return DDTREE_OK;
+  if (!parents || !mask || !depth || !tree_ok) return DDTREE_ERR_INVALID_ARG;
+  const uint64_t n = (uint64_t)B * N;
+  const uint64_t W = (uint64_t)(N + 31) / 32;
+  const Range ins[] = {range_of(parents, n * 4), range_of(prefix_offsets, prefix_offsets ? (B + 1) * 8ull : 0)};
+  const Range outs[] = {range_of(mask, n * W * 4), range_of(depth, n * 4), range_of(positions, positions ? n * 8 : 0),
+                        range_of(tree_ok, (uint64_t)B * 4)};
+  if (any_overlap(outs, 4, ins, 2)) return DDTREE_ERR_INVALID_ARG;
+  hipError_t e = launch_build_mask(parents, B, N, prefix_offsets, mask, depth, positions, tree_ok,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
+}
+
+int32_t ddtree_verify_attn_auto_splits(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
+                                       int64_t max_prefix_len) {
+  (void)Dl;
+  (void)Dr;
+  return auto_splits(dtype, B, N, H, max_prefix_len);
+}
+
+size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
+                                         int64_t max_prefix_len, int32_t num_splits) {
+  (void)Dr;
+  if (B <= 0 || N <= 0 || H <= 0 || Dl <= 0 || num_splits < 0) return 0;
+  const int s = resolve_splits(dtype, B, N, H, max_prefix_len, num_splits);
+  return workspace_bytes_for(dtype, B, N, H, Dl, s);
+}
+
+int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr, const void* q_lat,
+                       const void* q_rope, const void* ckv, int64_t ld_ckv, const void* krope, int64_t ld_krope,
+                       const int64_t* prefix_offsets, int64_t max_prefix_len, const void* ckv_tree,
+                       int64_t ld_ckv_tree, const void* krope_tree, int64_t ld_krope_tree, const uint32_t* mask,
+                       float softmax_scale, int32_t num_splits, float* o, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  // ---- shapes ----
+  if (dtype != DDTREE_F32 && dtype != DDTREE_BF16) return DDTREE_ERR_UNSUPPORTED;
+  if (B < 0 || N < 1 || H < 1 || Dl < 1 || Dr < 0 || num_splits < 0 || max_prefix_len < 0)
+    return DDTREE_ERR_INVALID_ARG;
+  if (N > DDTREE_MAX_NODES) return DDTREE_ERR_UNSUPPORTED;
+  if (dtype == DDTREE_BF16 && !bf16_shape_supported(Dl, Dr)) return DDTREE_ERR_UNSUPPORTED;
+  if (dtype == DDTREE_F32 && (Dl > 512 || Dr > 512)) return DDTREE_ERR_UNSUPPORTED;
+  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+    return DDTREE_ERR_INVALID_ARG;
+  if ((int64_t)B * N * H > INT32_MAX / 4) return DDTREE_ERR_UNSUPPORTED;
+  if (B == 0) return DDTREE_OK;
+  // ---- pointers and strides ----
+  if (!q_lat || !prefix_offsets || !ckv_tree || !mask || !o || !lse) return DDTREE_ERR_INVALID_ARG;
+  if (Dr > 0 && (!q_rope || !krope_tree)) return DDTREE_ERR_INVALID_ARG;
+  if (max_prefix_len > 0 && (!ckv || (Dr > 0 && !krope))) return DDTREE_ERR_INVALID_ARG;
+  if (ld_ckv < Dl || ld_ckv_tree < Dl || ld_krope < Dr || ld_krope_tree < Dr) return DDTREE_ERR_INVALID_ARG;
+  if (dtype == DDTREE_BF16) {
+    if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(ckv) || !aligned16(krope) || !aligned16(ckv_tree) ||
+        !aligned16(krope_tree) || !aligned16(o))
+      return DDTREE_ERR_INVALID_ARG;
+    if ((ld_ckv | ld_krope | ld_ckv_tree | ld_krope_tree) & 7) return DDTREE_ERR_INVALID_ARG;
+  }
+  // ---- workspace ----
+  const int splits = resolve_splits(dtype, B, N, H, max_prefix_len, num_splits);
+  if (splits > 1024) return DDTREE_ERR_UNSUPPORTED;
+  const size_t need = workspace_bytes_for(dtype, B, N, H, Dl, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DDTREE_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return DDTREE_ERR_INVALID_ARG;
+  // ---- aliasing (extents known on the host) ----
+  const uint64_t rows = (uint64_t)B * N * H;
+  const uint64_t es = dtype == DDTREE_BF16 ? 2 : 4;
+  const uint64_t W = (uint64_t)(N + 31) / 32;
+  const uint64_t tree_rows = (uint64_t)B * N;
+  const Range ins[] = {range_of(q_lat, rows * Dl * es),
+                       range_of(q_rope, Dr ? rows * Dr * es : 0),
+                       range_of(prefix_offsets, (B + 1) * 8ull),
+                       range_of(mask, tree_rows * W * 4),
+                       range_of(ckv_tree, ((tree_rows - 1) * ld_ckv_tree + Dl) * es),
+                       range_of(krope_tree, Dr ? ((tree_rows - 1) * ld_krope_tree + Dr) * es : 0)};
+  const Range outs[] = {range_of(o, rows * Dl * 4), range_of(lse, rows * 4), range_of(workspace, need)};
+  if (any_overlap(outs, 3, ins, 6)) return DDTREE_ERR_INVALID_ARG;
+
+  AttnArgs a;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.Dl = Dl;
+  a.Dr = Dr;
+  a.q_lat = q_lat;
+  a.q_rope = q_rope;
+  a.ckv = ckv;
+  a.ld_ckv = ld_ckv;
+  a.krope = krope;
+  a.ld_krope = ld_krope;
+  a.prefix_offsets = prefix_offsets;
+  a.ckv_tree = ckv_tree;
+  a.ld_ckv_tree = ld_ckv_tree;
+  a.krope_tree = krope_tree;
+  a.ld_krope_tree = ld_krope_tree;
+  a.mask = mask;
+  a.scale = softmax_scale;
+  a.splits = splits;
+  a.o = o;
+  a.lse = lse;
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  if (splits > 1) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (uint64_t)splits * rows * Dl;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == DDTREE_BF16) {
+    e = launch_verify_attn_bf16(a, s);
+    if (e == hipSuccess && splits > 1) e = launch_attn_combine(a, s);
+  } else {
+    e = launch_verify_attn_f32(a, s);
+  }
+  return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
+}
+
+int ddtree_greedy_accept(const float* logits, int64_t ld_logits, const int32_t* tokens, const int32_t* parents,
+                         int32_t B, int32_t N, int32_t V, int32_t* target_argmax, int32_t* accept_len,
+                         int32_t* accept_nodes, int32_t* commit_tokens, void* stream) {
+  if (B < 0 || N < 1 || V < 1 || ld_logits < V) return DDTREE_ERR_INVALID_ARG;
+  if (N > DDTREE_MAX_NODES) return DDTREE_ERR_UNSUPPORTED;
+  if ((int64_t)B * N > INT32_MAX) return DDTREE_ERR_UNSUPPORTED;
+  if (B == 0) return DDTREE_OK;
+  if (!logits || !tokens || !parents || !target_argmax || !accept_len || !accept_nodes || !commit_tokens)
+    return DDTREE_ERR_INVALID_ARG;
+  const uint64_t n = (uint64_t)B * N;
+  const Range ins[] = {range_of(logits, ((n - 1) * (uint64_t)ld_logits + V) * 4), range_of(tokens, n * 4),
+                       range_of(parents, n * 4)};
+  const Range outs[] = {range_of(target_argmax, n * 4), range_of(accept_len, (uint64_t)B * 4),
+                        range_of(accept_nodes, n * 4), range_of(commit_tokens, n * 4)};
+  if (any_overlap(outs, 4, ins, 3)) return DDTREE_ERR_INVALID_ARG;
+  hipError_t e = launch_accept(logits, ld_logits, tokens, parents, B, N, V, target_argmax, accept_len, accept_nodes,
+                               commit_tokens, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal declarations shared by the host entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ddtree {
+
+// ---- launchers (each enqueues on `stream`, returns the launch's hipError_t) ----
+
+hipError_t launch_build_mask(const int32_t* parents, int B, int N, const int64_t* prefix_offsets, uint32_t* mask,
+                             int32_t* depth, int64_t* positions, int32_t* tree_ok, hipStream_t stream);
+
+hipError_t launch_accept(const float* logits, int64_t ld_logits, const int32_t* tokens, const int32_t* parents, int B,
+                         int N, int V, int32_t* target_argmax, int32_t* accept_len, int32_t* accept_nodes,
+                         int32_t* commit_tokens, hipStream_t stream);
+
+struct AttnArgs {
+  int B, N, H, Dl, Dr;
+  const void* q_lat;
+  const void* q_rope;
+  const void* ckv;
+  int64_t ld_ckv;
+  const void* krope;
+  int64_t ld_krope;
+  const int64_t* prefix_offsets;
+  const void* ckv_tree;
+  int64_t ld_ckv_tree;
+  const void* krope_tree;
+  int64_t ld_krope_tree;
+  const uint32_t* mask;
+  float scale;
+  int splits;          // >= 1
+  float* o;
+  float* lse;
+  float* part_o;       // [splits][B*N*H][Dl]  (splits > 1)
+  float* part_lse;     // [splits][B*N*H]      (splits > 1)
+};
+
+// bf16 MFMA kernel for (Dl, Dr) = (512, 64)
+constexpr int kMfmaDl = 512;
+constexpr int kMfmaDr = 64;
+constexpr int kRowsPerBlock = 128;   // query rows (node, head) per workgroup
+constexpr int kKeysPerTile = 32;     // latent KV rows per LDS tile
+
+hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_verify_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace ddtree

@@ -1,0 +1,426 @@
+// Tree-verify attention, absorbed MLA form, bf16 inputs on gfx950 MFMA.
+//
+// What is computed (page "The Moment of Proof: Validating a Native CUDA
+// Speculative Decoding Engine", section "Input Knowledge Required": MLA in
+// absorb form, the draft tree verified in one forward under a custom mask;
+// page "The Moment of Proof: Running the Native DDTree Speculative Decoding
+// Engine", section "Input Knowledge Required": verify attention with
+// visibility masking): every (node, head) query row attends to its request's
+// cached latent rows plus its visible tree rows; key = [c | r] (576 wide),
+// value = c (512 wide); output o (float32, latent space) and the natural
+// log-sum-exp of the scaled scores.
+//
+// Design (MI355X / gfx950):
+//  * All H heads of all N tree nodes of a request read the same latent KV
+//    stream, so (node, head) pairs are the rows of a dense contraction.  A
+//    workgroup of 4 waves owns 128 rows; each wave 32 rows.
+//  * The 32 rows' absorbed queries stay in VGPRs for the whole kernel (36
+//    bf16x8 B-fragments, 144 VGPRs).
+//  * KV tiles of 32 keys x 576 bf16 are copied HBM -> LDS with direct-to-LDS
+//    16-byte loads into a 3-deep ring, with a 16-byte-chunk XOR swizzle that
+//    keeps both read patterns below bank-conflict free.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = key rows read with
+//    ds_read_b128, B = query fragments): each lane ends up holding 16 scores
+//    of ONE query row, so the online-softmax statistics are per-lane scalars
+//    and the row max needs a single cross-half exchange.
+//  * O^T += V^T P^T on the same MFMA: V^T fragments come straight from the
+//    row-major LDS tile through ds_read_b64_tr_b16 (transpose reads), and
+//    the probabilities, rounded to bf16, are already in the B-operand layout
+//    (no shuffle).  The 512 x 32 float32 accumulator (256 registers) again
+//    holds one row per lane, so rescaling is a per-lane multiply; it is done
+//    lazily, only when the running max grows by more than 2^8.
+//  * Prefix tiles first, then tree tiles; the ancestor mask is one 32-bit
+//    word per row per tree tile.  Long prefixes can be split across
+//    workgroups (flash-decoding); partials are merged by the combine kernel
+//    with the log-sum-exp weights.
+#include <cmath>
+
+#include "ddtree_internal.h"
+
+namespace ddtree {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr int DL = kMfmaDl;                 // 512
+constexpr int DR = kMfmaDr;                 // 64
+
+constexpr int KT = kKeysPerTile;            // 32 keys per tile
+constexpr int C_ROW = DL * 2;               // 1024 bytes: latent part of one key in LDS
+constexpr int R_ROW = DR * 2;               // 128 bytes: rotary part of one key in LDS
+constexpr int R_OFF = KT * C_ROW;           // rotary region after the 32 latent rows
+constexpr int TILE_BYTES = KT * (C_ROW + R_ROW);  // 36864
+constexpr int NBUF = 3;
+constexpr int ROWS = kRowsPerBlock;         // 128
+constexpr int NWAVES = 4;
+constexpr int C_LOADS_PER_WAVE = KT / NWAVES;   // 8 latent rows (1 KB each) per wave per tile
+constexpr int LOADS_PER_WAVE = C_LOADS_PER_WAVE + 1;  // + one 1 KB slice of the rotary region
+constexpr int MAXW = 8;                     // mask words per row (N <= 256)
+constexpr float kRescaleLog2 = 8.0f;        // lazy rescale threshold (log2 units)
+
+static_assert(KT * R_ROW == NWAVES * 1024, "rotary region must split into one 1 KB load per wave");
+static_assert(LOADS_PER_WAVE == 9, "the tile loop's vmcnt wait assumes 9 loads per wave per tile");
+
+// 16-byte-chunk swizzle of a key row in LDS (XOR of the chunk index's low 3
+// bits).  Key-fragment reads take 8 keys at one chunk; transpose reads take 4
+// consecutive keys x 2 adjacent chunks.  Rows are multiples of 128 bytes, so
+// with 32 banks x 4 bytes both patterns touch distinct bank groups.
+__device__ __forceinline__ int swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+
+struct TileSrc {
+  const uint16_t* c;   // latent rows of the tile's first key
+  const uint16_t* r;   // rotary rows of the tile's first key
+  int ldc, ldr;        // row strides (elements)
+  int count;           // valid keys in this tile (1..32)
+};
+
+__device__ __forceinline__ TileSrc tile_source(const AttnArgs& a, int b, int64_t p0, int64_t L, int n_pt, int t) {
+  TileSrc s;
+  if (t < n_pt) {
+    const int64_t row0 = p0 + (int64_t)t * KT;
+    s.c = static_cast<const uint16_t*>(a.ckv) + row0 * a.ld_ckv;
+    s.r = static_cast<const uint16_t*>(a.krope) + row0 * a.ld_krope;
+    s.ldc = (int)a.ld_ckv;
+    s.ldr = (int)a.ld_krope;
+    const int64_t rem = L - (int64_t)t * KT;
+    s.count = rem < KT ? (int)rem : KT;
+  } else {
+    const int node0 = (t - n_pt) * KT;
+    const int64_t row0 = (int64_t)b * a.N + node0;
+    s.c = static_cast<const uint16_t*>(a.ckv_tree) + row0 * a.ld_ckv_tree;
+    s.r = static_cast<const uint16_t*>(a.krope_tree) + row0 * a.ld_krope_tree;
+    s.ldc = (int)a.ld_ckv_tree;
+    s.ldr = (int)a.ld_krope_tree;
+    const int rem = a.N - node0;
+    s.count = rem < KT ? rem : KT;
+  }
+  return s;
+}
+
+// One direct-to-LDS 16-byte load per lane: LDS[lds_base + 16 * lane] <- gbase[voff].
+// Written as inline asm so that the compiler does not treat it as an LDS store
+// and serialise every later LDS read behind it; completion is tracked by the
+// explicit vmcnt waits in the tile loop (vmcnt counts every vector memory op
+// in issue order, so waits the compiler adds for its own loads stay correct).
+// M0 is written and consumed inside the one statement; nothing else in this
+// kernel uses M0.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gbase, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_base), "v"(voff), "s"(gbase)
+      : "memory");
+}
+
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+}
+
+// Issue this wave's direct-to-LDS 16-byte loads of one tile.  LDS tile layout:
+// latent rows [32][1024 B] then rotary rows [32][128 B]; 16-byte chunk p of a
+// row sits at physical chunk p ^ swz(key).  Wave w loads latent rows
+// w, w + 4, ..., w + 28 (one 64-lane load each: lane = physical chunk, so
+// the lane's global chunk is lane ^ swz(key)), and 1 KB of the rotary region
+// (keys 8 w .. 8 w + 7, lane = key * 8 + physical chunk).  Keys past the
+// tile's valid count re-read its last valid row (masked later).
+__device__ __forceinline__ void issue_tile_loads(const TileSrc& s, uint32_t lds_buf, int wave, int lane) {
+  // keys w + 4 i have swz = 2 w + (i & 1)
+  const uint32_t cb0 = (uint32_t)(lane ^ (2 * wave)) * 16u;
+#pragma unroll
+  for (int i = 0; i < C_LOADS_PER_WAVE; ++i) {
+    const int key = wave + NWAVES * i;                    // wave-uniform
+    const int kc = min(key, s.count - 1);
+    const uint16_t* row = s.c + (int64_t)kc * s.ldc;      // scalar address
+    lds_dma16(lds_buf + key * C_ROW, row, (i & 1) ? (cb0 ^ 16u) : cb0);
+  }
+  {
+    const int key = wave * 8 + (lane >> 3);
+    const int kc = min(key, s.count - 1);
+    const int p = (lane & 7) ^ swz(key);
+    lds_dma16(lds_buf + R_OFF + wave * 1024, s.r, (uint32_t)(kc * s.ldr + p * 8) * 2u);
+  }
+}
+
+// Byte offset in a tile of the K fragment for latent k-step s (< 32).
+__device__ __forceinline__ int kaddr(int kbase, int ksw, int s) {
+  return kbase + (s >> 2) * 128 + (((2 * (s & 3)) ^ ksw) << 4);
+}
+
+// V^T fragment of 16-key step ks and 32-dim block db: two transpose reads of
+// 4 keys each (keys 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3).  An odd db
+// sets bit 2 of the logical chunk, i.e. flips bit 6 of the byte offset.
+__device__ __forceinline__ bf16x8 load_vt(const unsigned char* buf, int voff, int ks, int db) {
+  const unsigned char* va = buf + ((db & 1) ? (voff ^ 64) : voff) + ks * 16 * C_ROW + (db >> 1) * 128;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * C_ROW));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+verify_attn_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char s_kv[NBUF * TILE_BYTES];
+  __shared__ uint32_t s_mask[ROWS][MAXW];
+  __shared__ __attribute__((aligned(16))) unsigned char s_qr[ROWS * R_ROW];   // rotary queries, swizzled rows
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int lane = tid & 63;
+  const int g = lane >> 5;          // which 8-wide k half of an MFMA operand
+  const int lr = lane & 31;         // row within the wave's 32 rows
+
+  // ---- work item: (request, row block, split) ----
+  const int n_rows = a.N * a.H;
+  const int n_rb = (n_rows + ROWS - 1) / ROWS;
+  int item = blockIdx.x;
+  const int split = item % a.splits;
+  item /= a.splits;
+  const int rb = item % n_rb;
+  const int b = item / n_rb;
+
+  const int64_t p0 = a.prefix_offsets[b];
+  int64_t L = a.prefix_offsets[b + 1] - p0;
+  if (L < 0) L = 0;
+  const int n_pt = (int)((L + KT - 1) / KT);
+  const int last_row = min(n_rows - 1, rb * ROWS + ROWS - 1);
+  const int n_tt = (last_row / a.H) / KT + 1;     // tree tiles that any row here can see
+  const int T = n_pt + n_tt;
+  const int t0 = (int)((int64_t)split * T / a.splits);
+  const int t1 = (int)((int64_t)(split + 1) * T / a.splits);
+
+  // ---- per-row mask words (LDS) ----
+  const int W = (a.N + 31) >> 5;
+  for (int e = tid; e < ROWS * MAXW; e += 256) {
+    const int rl = e / MAXW, w = e % MAXW;
+    const int r = rb * ROWS + rl;
+    uint32_t v = 0u;
+    if (r < n_rows && w < W) v = a.mask[((int64_t)b * a.N + r / a.H) * W + w];
+    s_mask[rl][w] = v;
+  }
+
+  // ---- query fragments: B operand, lane (lr, g) holds Q[row lr][16 s + 8 g .. +8] ----
+  // The 32 latent k-steps stay in VGPRs; the 4 rotary k-steps are staged in LDS
+  // (row rl, 16-byte chunk p at p ^ (rl & 7)) and read per tile.
+  const int r_loc = rb * ROWS + wave * 32 + lr;
+  const bool row_ok = r_loc < n_rows;
+  const int64_t grow = (int64_t)b * n_rows + (row_ok ? r_loc : 0);
+  const int row_local = wave * 32 + lr;
+  bf16x8 qf[DL / 16];
+  {
+    const bf16x8* ql = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q_lat) + grow * DL) + g;
+#pragma unroll
+    for (int s = 0; s < DL / 16; ++s) qf[s] = row_ok ? ql[2 * s] : bf16x8{};
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q_rope) + grow * DR);
+#pragma unroll
+    for (int c = g; c < DR / 8; c += 2) {
+      const bf16x8 v = row_ok ? qr[c] : bf16x8{};
+      *reinterpret_cast<bf16x8*>(s_qr + row_local * R_ROW + ((c ^ (row_local & 7)) << 4)) = v;
+    }
+  }
+
+  // ---- LDS addresses (lane constants) ----
+  // K fragment (A of S^T): key lr, logical chunk 2 s + g.  With s = 4 a + s',
+  // the swizzled chunk is 8 a + ((2 s' + g) ^ swz(lr)); the rotary steps
+  // (s >= 32) read the rotary row of key lr the same way.
+  const int kbase = lr * C_ROW;
+  const int ksw = g ^ swz(lr);              // (2 s' + g) ^ swz(lr) = 2 s' ^ ksw
+  // V^T fragment (A of O^T) by transpose read.  Lane = 16 G + 4 rr + cc reads key
+  // 16 ks + 4 g + rr (+8 for the second read), dims 32 db + 16 (G & 1) + 4 cc .. +3.
+  int voff;
+  {
+    const int G = lane >> 4;
+    const int rr = (lane >> 2) & 3;
+    const int cc = lane & 3;
+    const int vkey = 4 * g + rr;            // key within a 16-key step (low 3 bits fix the swizzle)
+    const int pl = 2 * (G & 1) + (cc >> 1); // low 3 bits of the logical chunk for even db
+    voff = vkey * C_ROW + ((pl ^ swz(vkey)) << 4) + (cc & 1) * 8;   // odd db: chunk bit 2 flips
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)s_kv;   // LDS byte address of the ring
+
+  // ---- accumulators and softmax state (one query row per lane) ----
+  f32x16 oacc[DL / 32];
+#pragma unroll
+  for (int db = 0; db < DL / 32; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;   // running max, log2 units
+  float l_run = 0.f;         // this lane's half of the row's exp-sum
+  const float c_log2 = a.scale * 1.4426950408889634f;
+
+  // ---- prologue: first two tiles in flight ----
+  if (t0 < t1) issue_tile_loads(tile_source(a, b, p0, L, n_pt, t0), lds0, wave, lane);
+  if (t0 + 1 < t1) issue_tile_loads(tile_source(a, b, p0, L, n_pt, t0 + 1), lds0 + TILE_BYTES, wave, lane);
+
+  for (int t = t0; t < t1; ++t) {
+    const int j = t - t0;
+    unsigned char* buf = s_kv + (j % NBUF) * TILE_BYTES;
+    wait_vmcnt_le(t + 1 < t1 ? LOADS_PER_WAVE : 0);   // this wave's loads of tile t are done
+    __syncthreads();   // tile t visible to all waves; every wave is done with tile t-1
+    if (t + 2 < t1)
+      issue_tile_loads(tile_source(a, b, p0, L, n_pt, t + 2), lds0 + ((j + 2) % NBUF) * TILE_BYTES, wave, lane);
+
+    // ---- S^T[key][row] = K . Q^T over 576 dims (fragment reads two steps ahead) ----
+    f32x16 sacc = f32x16{};
+    {
+      bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, 0));
+      bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, 1));
+#pragma unroll
+      for (int s = 0; s < DL / 16; ++s) {
+        const bf16x8 kf = (s & 1) ? kb1 : kb0;
+        if (s + 2 < DL / 16) {
+          const bf16x8 nx = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, s + 2));
+          if (s & 1) kb1 = nx; else kb0 = nx;
+        }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // rotary k-steps: key rows from the tile's rotary region, queries from s_qr
+#pragma unroll
+      for (int sr = 0; sr < DR / 16; ++sr) {
+        const int c = 2 * sr + g;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(buf + R_OFF + lr * R_ROW + ((c ^ swz(lr)) << 4));
+        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(s_qr + row_local * R_ROW + ((c ^ (row_local & 7)) << 4));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- mask + online softmax.  sacc[4 jj + i] is key 8 jj + 4 g + i of row lr ----
+    // scores to log2 units, masked keys to -inf (in place)
+    if (t < n_pt) {
+      const int count = (int)min<int64_t>(L - (int64_t)t * KT, KT);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = 8 * (e >> 2) + 4 * g + (e & 3);
+        sacc[e] = key < count ? sacc[e] * c_log2 : -INFINITY;
+      }
+    } else {
+      const uint32_t word = s_mask[row_local][t - n_pt] >> (4 * g);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = 8 * (e >> 2) + (e & 3);          // + 4 g, folded into the shift above
+        sacc[e] = ((word >> key) & 1u) ? sacc[e] * c_log2 : -INFINITY;
+      }
+    }
+    float mx = sacc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const bool need = m_new > m_run + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      m_run = need ? m_new : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DL / 32; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sacc[e] - m_use);
+      l_run += p;
+      pb[e >> 3][e & 7] = (__bf16)p;
+    }
+
+    // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row] (fragment reads one step ahead) ----
+    {
+      bf16x8 vnext = load_vt(buf, voff, 0, 0);
+#pragma unroll
+      for (int st = 0; st < 2 * (DL / 32); ++st) {
+        const int ks = st / (DL / 32), db = st % (DL / 32);
+        const bf16x8 vf = vnext;
+        if (st + 1 < 2 * (DL / 32)) vnext = load_vt(buf, voff, (st + 1) / (DL / 32), (st + 1) % (DL / 32));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], oacc[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+  float* orow;
+  float* lrow;
+  if (a.splits == 1) {
+    orow = a.o + grow * DL;
+    lrow = a.lse + grow;
+  } else {
+    const int64_t total_rows = (int64_t)a.B * n_rows;
+    orow = a.part_o + ((int64_t)split * total_rows + grow) * DL;
+    lrow = a.part_lse + (int64_t)split * total_rows + grow;
+  }
+  // oacc[db][4 jj + i] is dim 32 db + 8 jj + 4 g + i of row lr
+#pragma unroll
+  for (int db = 0; db < DL / 32; ++db) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float4 v;
+      v.x = oacc[db][4 * jj + 0] * inv_l;
+      v.y = oacc[db][4 * jj + 1] * inv_l;
+      v.z = oacc[db][4 * jj + 2] * inv_l;
+      v.w = oacc[db][4 * jj + 3] * inv_l;
+      *reinterpret_cast<float4*>(orow + 32 * db + 8 * jj + 4 * g) = v;
+    }
+  }
+  if (g == 0) *lrow = lse;
+}
+
+// Merge split partials: lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.
+__global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse, int splits,
+                                                           int64_t total_rows, int Dl, float* __restrict__ o,
+                                                           float* __restrict__ lse) {
+  const int per_row = Dl / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = idx / per_row;
+  const int c4 = (int)(idx - row * per_row);
+  if (row >= total_rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_lse[s * total_rows + row]);
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < splits; ++s) {
+    const float ls = part_lse[s * total_rows + row];
+    if (ls == -INFINITY) continue;
+    const float w = expf(ls - mx);
+    wsum += w;
+    const float4 v = reinterpret_cast<const float4*>(part_o + (s * total_rows + row) * Dl)[c4];
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float inv = 1.f / wsum;
+  reinterpret_cast<float4*>(o + row * Dl)[c4] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (c4 == 0) lse[row] = mx + logf(wsum);
+}
+
+}  // namespace
+
+hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream) {
+  if (a.B == 0) return hipSuccess;
+  const int n_rb = (a.N * a.H + ROWS - 1) / ROWS;
+  const int grid = a.B * n_rb * a.splits;
+  hipLaunchKernelGGL(verify_attn_bf16_kernel, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream) {
+  const int64_t total_rows = (int64_t)a.B * a.N * a.H;
+  const int64_t threads = total_rows * (a.Dl / 4);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.part_o, a.part_lse,
+                     a.splits, total_rows, a.Dl, a.o, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace ddtree

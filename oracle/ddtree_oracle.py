@@ -106,7 +106,7 @@ def visible_nodes(mask_row: np.ndarray, n: int) -> list:
 # Tree-verify attention, absorbed MLA form
 # ----------------------------------------------------------------------------
 
-def verify_attn_ref(q_lat, q_rope, ckv, krope, prefix_offsets, ckv_tree, krope_tree, mask, scale):
+def verify_attn_ref(q_lat, q_rope, ckv, krope, prefix_offsets, ckv_tree, krope_tree, mask, scale, nodes=None):
     """Attention of every tree node over the shared prefix plus its visible tree nodes.
 
     For request b, node i and head h, the key set J is the cached prefix rows
@@ -123,6 +123,8 @@ def verify_attn_ref(q_lat, q_rope, ckv, krope, prefix_offsets, ckv_tree, krope_t
       q_lat [B,N,H,Dl], q_rope [B,N,H,Dr], ckv [T,Dl], krope [T,Dr],
       prefix_offsets int [B+1], ckv_tree [B,N,Dl], krope_tree [B,N,Dr],
       mask uint32 [B,N,W].
+    nodes: optional list of (b, i) pairs to compute (others stay 0), for
+    sampling large workloads; the arithmetic per node is unchanged.
     Returns o float64 [B,N,H,Dl], lse float64 [B,N,H].
     """
     q_lat = np.asarray(q_lat, dtype=np.float64)
@@ -130,11 +132,16 @@ def verify_attn_ref(q_lat, q_rope, ckv, krope, prefix_offsets, ckv_tree, krope_t
     B, N, H, Dl = q_lat.shape
     o = np.zeros((B, N, H, Dl), dtype=np.float64)
     lse = np.zeros((B, N, H), dtype=np.float64)
+    wanted = None if nodes is None else {(int(b), int(i)) for b, i in nodes}
     for b in range(B):
+        if wanted is not None and not any(wb == b for wb, _ in wanted):
+            continue
         s0, s1 = int(prefix_offsets[b]), int(prefix_offsets[b + 1])
         C_prefix = np.asarray(ckv[s0:s1], dtype=np.float64)
         R_prefix = np.asarray(krope[s0:s1], dtype=np.float64)
         for i in range(N):
+            if wanted is not None and (b, i) not in wanted:
+                continue
             vis = visible_nodes(mask[b, i], N)
             C = np.concatenate([C_prefix, np.asarray(ckv_tree[b, vis], dtype=np.float64)], axis=0)
             R = np.concatenate([R_prefix, np.asarray(krope_tree[b, vis], dtype=np.float64)], axis=0)

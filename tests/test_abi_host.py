@@ -1,0 +1,160 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared symbol,
+and rejects invalid calls on the host before any HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_tree_verify_absorb_amd as dd
+from mla_tree_verify_absorb_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddtree.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = dd.DDTREE_OK, dd.DDTREE_ERR_INVALID_ARG, dd.DDTREE_ERR_UNSUPPORTED, \
+    dd.DDTREE_ERR_WORKSPACE
+F32, BF16 = dd.DDTREE_F32, dd.DDTREE_BF16
+A = 0x10000      # fake, 16-byte aligned "device" addresses: never dereferenced by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddtree_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("ddtree_build_mask", "ddtree_verify_attn", "ddtree_greedy_accept"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dd.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding's signature table covers all of them
+    assert set(declared_functions()) == set(_lib._SIGNATURES)
+
+
+def test_status_strings():
+    assert dd.ddtree_status_string(OK) == "DDTREE_OK"
+    assert dd.ddtree_status_string(INVALID) == "DDTREE_ERR_INVALID_ARG"
+    assert dd.ddtree_status_string(UNSUPPORTED) == "DDTREE_ERR_UNSUPPORTED"
+    assert dd.ddtree_status_string(WORKSPACE) == "DDTREE_ERR_WORKSPACE"
+    assert dd.ddtree_status_string(dd.DDTREE_ERR_HIP) == "DDTREE_ERR_HIP"
+    assert dd.ddtree_status_string(12345) == "DDTREE_UNKNOWN_STATUS"
+
+
+# ---------------------------------------------------------------- build_mask
+
+def bm(parents=A, B=2, N=8, offs=A + 4096, mask=A + 8192, depth=A + 12288, pos=A + 16384, ok=A + 20480):
+    return dd.lib().ddtree_build_mask(parents, B, N, offs, mask, depth, pos, ok, None)
+
+
+def test_build_mask_rejects_bad_shapes_and_pointers():
+    assert bm(N=0) == INVALID
+    assert bm(B=-1) == INVALID
+    assert bm(N=257) == UNSUPPORTED
+    assert bm(B=0) == OK                      # nothing to do, nothing enqueued
+    assert bm(parents=None) == INVALID
+    assert bm(mask=None) == INVALID
+    assert bm(depth=None) == INVALID
+    assert bm(ok=None) == INVALID
+    assert bm(mask=A + 16) == INVALID          # mask overlaps parents
+    assert bm(depth=A + 8192 + 32) == INVALID  # depth overlaps mask
+    assert bm(pos=A + 4096) == INVALID         # positions overlap prefix_offsets
+
+
+# ---------------------------------------------------------------- verify_attn
+
+def attn(dtype=BF16, B=1, N=8, H=64, Dl=512, Dr=64, q=A, qr=A + (1 << 24), ckv=A + (2 << 24), ld_ckv=576,
+         krope=A + (2 << 24) + 1024, ld_krope=576, offs=A + (3 << 24), max_len=64, ckv_t=A + (4 << 24),
+         ld_ckv_t=576, krope_t=A + (4 << 24) + 1024, ld_krope_t=576, mask=A + (5 << 24), scale=0.07,
+         splits=1, o=A + (6 << 24), lse=A + (7 << 24), ws=None, ws_bytes=0):
+    return dd.lib().ddtree_verify_attn(dtype, B, N, H, Dl, Dr, q, qr, ckv, ld_ckv, krope, ld_krope, offs, max_len,
+                                       ckv_t, ld_ckv_t, krope_t, ld_krope_t, mask, scale, splits, o, lse, ws,
+                                       ws_bytes, None)
+
+
+def test_verify_attn_shape_support():
+    assert attn(dtype=7) == UNSUPPORTED
+    assert attn(Dl=256) == UNSUPPORTED                 # bf16 kernel is (512, 64)
+    assert attn(Dr=32) == UNSUPPORTED
+    assert attn(dtype=F32, Dl=1024) == UNSUPPORTED
+    assert attn(N=257) == UNSUPPORTED
+    assert attn(N=0) == INVALID
+    assert attn(H=0) == INVALID
+    assert attn(B=-2) == INVALID
+    assert attn(B=0) == OK
+
+
+def test_verify_attn_rejects_bad_pointers_strides_and_scale():
+    assert attn(q=None) == INVALID
+    assert attn(mask=None) == INVALID
+    assert attn(o=None) == INVALID
+    assert attn(ckv=None) == INVALID                  # a nonempty prefix needs a cache
+    assert attn(ld_ckv=500) == INVALID                # row stride shorter than a row
+    assert attn(ld_krope=60) == INVALID
+    assert attn(ld_ckv=580) == INVALID                # bf16 rows must be 16-byte multiples
+    assert attn(ckv=A + (2 << 24) + 2) == INVALID     # misaligned bf16 base
+    assert attn(scale=float("nan")) == INVALID
+    assert attn(scale=float("inf")) == INVALID
+
+
+def test_verify_attn_rejects_aliasing():
+    assert attn(o=A + 64) == INVALID                  # o overlaps q_lat
+    assert attn(lse=A + (6 << 24) + 4096) == INVALID  # lse overlaps o
+    assert attn(o=A + (5 << 24)) == INVALID           # o overlaps mask
+
+
+def test_workspace_contract():
+    lib = dd.lib()
+    # splits = 1 needs no workspace; S > 1 needs S * rows * (Dl + 1) floats
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 8, 64, 512, 64, 4096, 1) == 0
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 8, 64, 512, 64, 4096, 4) == 4 * 8 * 64 * 513 * 4
+    assert lib.ddtree_verify_attn_workspace_size(F32, 1, 8, 4, 64, 32, 4096, 4) == 0   # fp32 path never splits
+    assert attn(splits=4) == WORKSPACE
+    assert attn(splits=4, ws=A + (8 << 24), ws_bytes=4 * 8 * 64 * 513 * 4 - 4) == WORKSPACE
+    assert attn(splits=4, ws=A + (8 << 24) + 8, ws_bytes=4 * 8 * 64 * 513 * 4) == INVALID   # misaligned
+    assert attn(splits=-1) == INVALID
+
+
+def test_auto_split_heuristic():
+    lib = dd.lib()
+    # one request of 64 nodes x 64 heads = 32 row blocks: 8 splits cover 256 CUs
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 64, 64, 512, 64, 4096) == 8
+    # 4 x 128 nodes x 64 heads = 256 row blocks: no split
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 4, 128, 64, 512, 64, 131072) == 1
+    # short prefixes are not split below 4 tiles per split
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 32) == 1
+    assert lib.ddtree_verify_attn_auto_splits(F32, 1, 8, 4, 64, 32, 4096) == 1
+    ws = lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 0)
+    assert ws == 8 * 64 * 64 * 513 * 4
+
+
+# ---------------------------------------------------------------- greedy_accept
+
+def acc(logits=A, ld=512, tokens=A + (1 << 24), parents=A + (1 << 24) + 4096, B=1, N=8, V=512,
+        tstar=A + (2 << 24), alen=A + (2 << 24) + 4096, nodes=A + (2 << 24) + 8192, commit=A + (2 << 24) + 12288):
+    return dd.lib().ddtree_greedy_accept(logits, ld, tokens, parents, B, N, V, tstar, alen, nodes, commit, None)
+
+
+def test_greedy_accept_validation():
+    assert acc(V=0) == INVALID
+    assert acc(ld=100) == INVALID                      # ld < V
+    assert acc(N=0) == INVALID
+    assert acc(N=300) == UNSUPPORTED
+    assert acc(B=0) == OK
+    assert acc(logits=None) == INVALID
+    assert acc(commit=None) == INVALID
+    assert acc(tstar=A + 100) == INVALID               # overlaps logits
+    assert acc(nodes=A + (2 << 24) + 4) == INVALID     # overlaps target_argmax
+
+
+def test_binding_refuses_without_library(monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "_LIB_PATH", "/nonexistent/libddtree.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
