@@ -1,0 +1,254 @@
+"""Benchmark of the DDTree tree-verify hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+ddtree_build_mask -> ddtree_verify_attn (bf16 MFMA, + split merge when split)
+-> ddtree_greedy_accept (vocab argmax + path walk).  Default workload: Kimi-K2
+shapes with a long context and the accept step -- 4 requests x 128-node draft
+trees x 64 heads, kv_lora 512 + rope 64, 131072-token cached prefixes, logits
+[4, 128, 163840] float32.  Inputs are seeded synthetic draws, resident in HBM
+before the timed region.
+
+Prints one JSON line.  `value` is the algorithmic attention TFLOP/s over the
+whole step (mask + attention + accept); the per-kernel figures, the roofline
+of the dominant kernel (the bf16 attention kernel, timed with HIP events on
+its launch stream) and the CPU oracle baseline on a bounded sample are in the
+same line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
+ATTN_KERNEL = "verify_attn_bf16_kernel"
+ATTN_SOURCE = os.path.join(ROOT, "mla_tree_verify_absorb_amd", "csrc", "verify_attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_bf16_k2_long_context_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5, help="workload number (3, 4 or 5); 5 is the headline")
+    ap.add_argument("--splits", type=int, default=0, help="KV splits (0 = library's automatic choice)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB --steps times (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate HBM traffic."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": steps}), flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_work(w, depth):
+    """Attention flops / bytes and accept bytes of one step (see the design notes)."""
+    import numpy as np
+    vis = (w.prefix_lens[:, None] + depth.astype(np.int64) + 1)          # keys seen by each node
+    keys_total = int(vis.sum())
+    flops = 2 * w.H * (2 * w.Dl + w.Dr) * keys_total
+    esz = 2 if w.dtype == "bf16" else 4
+    rows = w.B * w.N * w.H
+    attn_bytes = (int(w.prefix_lens.sum()) * (w.Dl + w.Dr) * esz           # prefix KV read once
+                  + w.B * w.N * (w.Dl + w.Dr) * esz                         # tree KV
+                  + rows * (w.Dl + w.Dr) * esz                              # queries
+                  + rows * w.Dl * 4 + rows * 4                              # o, lse
+                  + w.B * w.N * ((w.N + 31) // 32) * 4)                     # mask
+    accept_bytes = w.B * w.N * w.V * 4 if w.V else 0
+    return flops, attn_bytes, accept_bytes
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, on request 0's first n nodes (all heads, full prefix)."""
+    import numpy as np
+    from oracle import build_mask_ref, verify_attn_ref
+    from synth import restrict
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    f = w.f32
+    kv = f("kv")
+    kt = f("kv_tree")
+    done_flops = 0
+    elapsed = 0.0
+    n_done = 0
+    n = 1
+    while n <= w.N and elapsed < budget_s:
+        sub = restrict(w, 0, n)
+        mask, depth, _, _ = build_mask_ref(sub.parents, sub.prefix_lens)
+        L = int(sub.prefix_lens[0])
+        node = n - 1                                   # time node n-1 alone over the full prefix
+        t0 = time.perf_counter()
+        verify_attn_ref(f("q_lat")[:1, :n], f("q_rope")[:1, :n], kv[:L, :w.Dl], kv[:L, w.Dl:], sub.prefix_offsets,
+                        kt[:1, :n, :w.Dl], kt[:1, :n, w.Dl:], mask, w.scale, nodes=[(0, node)])
+        elapsed += time.perf_counter() - t0
+        done_flops += 2 * w.H * (2 * w.Dl + w.Dr) * (L + int(depth[0, node]) + 1)
+        n_done += 1
+        n += 1
+    return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"request 0, tree nodes 0..{n_done - 1} one at a time (all {w.H} heads), full "
+                      f"{int(w.prefix_lens[0])}-token prefix, float64 NumPy; {elapsed:.1f} s of oracle time",
+            "seconds": round(elapsed, 2)}
+
+
+def traffic_for_current_kernel(launch_flops):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash(ATTN_SOURCE) or t.get("launch_flops") != launch_flops:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding is a design note, "
+              f"not part of this build", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb, args.steps)
+        return
+    import numpy as np
+    import torch
+
+    import mla_tree_verify_absorb_amd as dd
+    from synth import CONFIGS, make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    w = make_config(args.config)
+    gen_s = time.perf_counter() - t_gen
+
+    def to_dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    parents = torch.from_numpy(w.parents).to(dev)
+    offsets = torch.from_numpy(w.prefix_offsets).to(dev)
+    q_lat, q_rope = to_dev(w.q_lat), to_dev(w.q_rope)
+    kv, kv_tree = to_dev(w.kv), to_dev(w.kv_tree)
+    ckv, krope = kv[:, :w.Dl], kv[:, w.Dl:]
+    ckv_t, krope_t = kv_tree[..., :w.Dl], kv_tree[..., w.Dl:]
+    logits = torch.from_numpy(w.logits).to(dev) if w.logits is not None else None
+    tokens = torch.from_numpy(w.tokens).to(dev) if w.tokens is not None else None
+    max_len = int(w.prefix_lens.max())
+    code = dd.DDTREE_BF16 if w.dtype == "bf16" else dd.DDTREE_F32
+    splits = args.splits or dd.ddtree_verify_attn_auto_splits(code, w.B, w.N, w.H, w.Dl, w.Dr, max_len)
+    ws_bytes = dd.ddtree_verify_attn_workspace_size(code, w.B, w.N, w.H, w.Dl, w.Dr, max_len, splits)
+    workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    W = (w.N + 31) // 32
+    mask = torch.empty((w.B, w.N, W), dtype=torch.int32, device=dev)
+    depth = torch.empty((w.B, w.N), dtype=torch.int32, device=dev)
+    positions = torch.empty((w.B, w.N), dtype=torch.int64, device=dev)
+    tree_ok = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    o = torch.empty((w.B, w.N, w.H, w.Dl), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.N, w.H), dtype=torch.float32, device=dev)
+    acc_out = None
+    if logits is not None:
+        acc_out = [torch.empty((w.B, w.N), dtype=torch.int32, device=dev), torch.empty((w.B,), dtype=torch.int32,
+                   device=dev), torch.empty((w.B, w.N), dtype=torch.int32, device=dev),
+                   torch.empty((w.B, w.N), dtype=torch.int32, device=dev)]
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(timed):
+        if timed:
+            ev[0].record(stream)
+        dd.ddtree_build_mask(parents, offsets, mask=mask, depth=depth, positions=positions, tree_ok=tree_ok)
+        if timed:
+            ev[1].record(stream)
+        dd.ddtree_verify_attn(q_lat, q_rope, ckv, krope, offsets, max_len, ckv_t, krope_t, mask, w.scale,
+                              num_splits=splits, o=o, lse=lse, workspace=workspace)
+        if timed:
+            ev[2].record(stream)
+        if logits is not None:
+            dd.ddtree_greedy_accept(logits, tokens, parents, target_argmax=acc_out[0], accept_len=acc_out[1],
+                                    accept_nodes=acc_out[2], commit_tokens=acc_out[3])
+        if timed:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t_mask = t_attn = t_acc = 0.0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        ev[3].synchronize()
+        t_mask += ev[0].elapsed_time(ev[1])
+        t_attn += ev[1].elapsed_time(ev[2])
+        t_acc += ev[2].elapsed_time(ev[3])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    K = args.steps
+    mask_ms, attn_ms, acc_ms = t_mask / K, t_attn / K, t_acc / K
+    step_ms = mask_ms + attn_ms + acc_ms
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), "non-finite attention output"
+    assert int(tree_ok.min()) == 1
+
+    flops, attn_bytes, accept_bytes = algorithmic_work(w, depth.cpu().numpy())
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    value = flops / (step_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_for_current_kernel(flops), "kernel": ATTN_KERNEL,
+                "launch_ms": round(attn_ms, 4), "algorithmic_flops": flops, "algorithmic_bytes": attn_bytes}
+    out = {
+        "metric": "tree-verify attn TFLOP/s & HBM GB/s (% roofline); verify steps/sec at K2 shape",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": CONFIGS[args.config]["name"], "batch": w.B, "tree_nodes": w.N, "heads": w.H,
+                   "kv_lora": w.Dl, "rope_dim": w.Dr, "prefix_len_max": max_len,
+                   "prefix_len_total": int(w.prefix_lens.sum()), "vocab": w.V, "kv_splits": splits},
+        "verify_steps_per_s": round(1e3 / step_ms, 2),
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_hbm_gbps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
+        "mask_ms": round(mask_ms, 4), "attn_ms": round(attn_ms, 4), "accept_ms": round(acc_ms, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": roofline,
+    }
+    if accept_bytes:
+        gbps = accept_bytes / (acc_ms * 1e-3) / 1e9
+        out["accept_hbm_gbps"] = round(gbps, 1)
+        out["accept_hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    out["input_generation_s"] = round(gen_s, 1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
