@@ -14,11 +14,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libddtree.so")
 SOURCES = ["ddtree_api.hip", "build_mask.hip", "accept.hip", "verify_attn_f32.hip", "verify_attn_bf16.hip"]
-# Per-file device flags.  The bf16 attention kernel keeps a 512 x 32 float32
-# accumulator per wave: with MFMA results in the VGPR form the register
-# allocator places the long-lived accumulators and query fragments in AGPRs
-# itself and the kernel needs no scratch.
-FILE_FLAGS = {"verify_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file device flags (none at present).
+FILE_FLAGS = {}
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for all device code (the compiler

@@ -27,8 +27,13 @@
 //    row-major LDS tile through ds_read_b64_tr_b16 (transpose reads), and
 //    the probabilities, rounded to bf16, are already in the B-operand layout
 //    (no shuffle).  The 512 x 32 float32 accumulator (256 registers) again
-//    holds one row per lane, so rescaling is a per-lane multiply; it is done
-//    lazily, only when the running max grows by more than 2^8.
+//    holds one row per lane.  Probabilities use a fixed per-row reference
+//    (the first visible tile's max, with 2^100 of headroom), so the
+//    accumulators are never rescaled; a score beyond the headroom triggers
+//    one rerun of the workgroup's tiles with the true row maximum.
+//  * MFMAs are issued by inline asm to pin S^T to VGPRs and O^T to AGPRs;
+//    LDS fragment reads run 4 MFMAs ahead; workgroups are mapped so that a
+//    request's row blocks share one XCD's L2.
 //  * Prefix tiles first, then tree tiles; the ancestor mask is one 32-bit
 //    word per row per tree tile.  Long prefixes can be split across
 //    workgroups (flash-decoding); partials are merged by the combine kernel
@@ -60,7 +65,7 @@ constexpr int NWAVES = 4;
 constexpr int C_LOADS_PER_WAVE = KT / NWAVES;   // 8 latent rows (1 KB each) per wave per tile
 constexpr int LOADS_PER_WAVE = C_LOADS_PER_WAVE + 1;  // + one 1 KB slice of the rotary region
 constexpr int MAXW = 8;                     // mask words per row (N <= 256)
-constexpr float kRescaleLog2 = 8.0f;        // lazy rescale threshold (log2 units)
+constexpr float kHeadroomLog2 = 100.0f;     // scores may exceed a row's reference by 2^100
 
 static_assert(KT * R_ROW == NWAVES * 1024, "rotary region must split into one 1 KB load per wave");
 static_assert(LOADS_PER_WAVE == 9, "the tile loop's vmcnt wait assumes 9 loads per wave per tile");
@@ -163,6 +168,72 @@ __device__ __forceinline__ bf16x8 load_vt(const unsigned char* buf, int voff, in
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// ---- MFMA issue (inline asm) ---------------------------------------------
+// The MFMAs are issued through inline asm so that the two accumulators get the
+// register class each needs: S^T (read by the softmax VALU code) in VGPRs and
+// the 512 x 32 output accumulator in AGPRs.  The compiler does not model the
+// MFMA pipeline behind an asm statement, so the wait states it would insert
+// are written out: 16 after the last S^T MFMA of a tile before VALU reads of
+// S^T, 16 after the last O^T MFMA of a tile before any AGPR read, and 4
+// between the VALU writes of P (and of rescaled AGPRs) and the first O^T
+// MFMA.  Chained MFMAs on one accumulator need no wait states.
+__device__ __forceinline__ void mfma_s_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7"
+      : "+v"(acc)
+      : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile(
+      "s_nop 3\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+      : "+a"(acc)
+      : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7"
+      : "+a"(acc)
+      : "v"(a), "v"(b));
+}
+
+// max / sum of a value and its twin in the other half-wave (same query row)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8).
+// Give each XCD a contiguous range of work items, so the row blocks of one
+// request (which stream the same KV) share an L2.
+__device__ __forceinline__ int xcd_local_item(int block, int total) {
+  const int x = block & 7, k = block >> 3;
+  const int base = total >> 3, extra = total & 7;
+  return x * base + min(x, extra) + k;
+}
+
+constexpr int KRING = 4;   // K-fragment reads in flight ahead of the S^T MFMAs
+constexpr int VRING = 4;   // V^T-fragment reads in flight ahead of the O^T MFMAs
+
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 verify_attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char s_kv[NBUF * TILE_BYTES];
@@ -178,7 +249,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
   // ---- work item: (request, row block, split) ----
   const int n_rows = a.N * a.H;
   const int n_rb = (n_rows + ROWS - 1) / ROWS;
-  int item = blockIdx.x;
+  int item = xcd_local_item(blockIdx.x, gridDim.x);
   const int split = item % a.splits;
   item /= a.splits;
   const int rb = item % n_rb;
@@ -215,11 +286,15 @@ verify_attn_bf16_kernel(AttnArgs a) {
   {
     const bf16x8* ql = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q_lat) + grow * DL) + g;
 #pragma unroll
-    for (int s = 0; s < DL / 16; ++s) qf[s] = row_ok ? ql[2 * s] : bf16x8{};
+    for (int s = 0; s < DL / 16; ++s) {
+      const bf16x8 v = ql[2 * s];
+      qf[s] = row_ok ? v : bf16x8{};
+    }
     const bf16x8* qr = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q_rope) + grow * DR);
 #pragma unroll
     for (int c = g; c < DR / 8; c += 2) {
-      const bf16x8 v = row_ok ? qr[c] : bf16x8{};
+      const bf16x8 v0 = qr[c];
+      const bf16x8 v = row_ok ? v0 : bf16x8{};
       *reinterpret_cast<bf16x8*>(s_qr + row_local * R_ROW + ((c ^ (row_local & 7)) << 4)) = v;
     }
   }
@@ -242,14 +317,28 @@ verify_attn_bf16_kernel(AttnArgs a) {
     voff = vkey * C_ROW + ((pl ^ swz(vkey)) << 4) + (cc & 1) * 8;   // odd db: chunk bit 2 flips
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)s_kv;   // LDS byte address of the ring
+  const unsigned char* qr_row = s_qr + row_local * R_ROW;
 
   // ---- accumulators and softmax state (one query row per lane) ----
+  // Each row's probabilities are taken relative to a fixed reference m_ref:
+  // the maximum score of the first tile in which the row sees any key (the
+  // output and the exp-sum are exactly zero before that, so nothing needs
+  // rescaling).  Later scores may exceed the reference by up to 2^100, which
+  // bf16 P and the float32 accumulators hold without overflow, so the
+  // accumulators are never rescaled.  Should a score exceed that headroom,
+  // the workgroup runs its tiles once more with the row's true maximum
+  // (tracked in m_max) as the reference; that pass cannot overflow.
   f32x16 oacc[DL / 32];
-#pragma unroll
-  for (int db = 0; db < DL / 32; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;   // running max, log2 units
+  float m_ref = -INFINITY;   // reference max, log2 units
+  float m_max = -INFINITY;   // true max of the scores seen, log2 units
   float l_run = 0.f;         // this lane's half of the row's exp-sum
   const float c_log2 = a.scale * 1.4426950408889634f;
+
+  for (int pass = 0; pass < 2; ++pass) {
+  bool overflow = false;
+  l_run = 0.f;
+#pragma unroll
+  for (int db = 0; db < DL / 32; ++db) oacc[db] = f32x16{};
 
   // ---- prologue: first two tiles in flight ----
   if (t0 < t1) issue_tile_loads(tile_source(a, b, p0, L, n_pt, t0), lds0, wave, lane);
@@ -257,96 +346,108 @@ verify_attn_bf16_kernel(AttnArgs a) {
 
   for (int t = t0; t < t1; ++t) {
     const int j = t - t0;
-    unsigned char* buf = s_kv + (j % NBUF) * TILE_BYTES;
+    const unsigned char* buf = s_kv + (j % NBUF) * TILE_BYTES;
     wait_vmcnt_le(t + 1 < t1 ? LOADS_PER_WAVE : 0);   // this wave's loads of tile t are done
     __syncthreads();   // tile t visible to all waves; every wave is done with tile t-1
-    if (t + 2 < t1)
-      issue_tile_loads(tile_source(a, b, p0, L, n_pt, t + 2), lds0 + ((j + 2) % NBUF) * TILE_BYTES, wave, lane);
+    if (t + 2 < t1) issue_tile_loads(tile_source(a, b, p0, L, n_pt, t + 2), lds0 + ((j + 2) % NBUF) * TILE_BYTES,
+                                     wave, lane);
 
-    // ---- S^T[key][row] = K . Q^T over 576 dims (fragment reads two steps ahead) ----
-    f32x16 sacc = f32x16{};
+    // ---- S^T[key][row] = K . Q^T over 576 dims; K-fragment reads KRING steps ahead ----
+    f32x16 sacc;
     {
-      bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, 0));
-      bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, 1));
+      bf16x8 kring[KRING];
+      bf16x8 qrr[DR / 16];
 #pragma unroll
-      for (int s = 0; s < DL / 16; ++s) {
-        const bf16x8 kf = (s & 1) ? kb1 : kb0;
-        if (s + 2 < DL / 16) {
-          const bf16x8 nx = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, s + 2));
-          if (s & 1) kb1 = nx; else kb0 = nx;
+      for (int s = 0; s < KRING; ++s) kring[s] = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, s));
+#pragma unroll
+      for (int s = 0; s < DL / 16 + DR / 16; ++s) {
+        const bf16x8 kf = kring[s % KRING];
+        const int nx = s + KRING;
+        if (nx < DL / 16) {
+          kring[s % KRING] = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, nx));
+        } else if (nx < DL / 16 + DR / 16) {
+          // rotary steps: key rows from the tile's rotary region, queries from s_qr
+          const int c = 2 * (nx - DL / 16) + g;
+          kring[s % KRING] = *reinterpret_cast<const bf16x8*>(buf + R_OFF + lr * R_ROW + ((c ^ swz(lr)) << 4));
+          qrr[nx - DL / 16] = *reinterpret_cast<const bf16x8*>(qr_row + ((c ^ (row_local & 7)) << 4));
         }
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // rotary k-steps: key rows from the tile's rotary region, queries from s_qr
-#pragma unroll
-      for (int sr = 0; sr < DR / 16; ++sr) {
-        const int c = 2 * sr + g;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(buf + R_OFF + lr * R_ROW + ((c ^ swz(lr)) << 4));
-        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(s_qr + row_local * R_ROW + ((c ^ (row_local & 7)) << 4));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, sacc, 0, 0, 0);
+        const bf16x8 qv = s < DL / 16 ? qf[s] : qrr[s - DL / 16];
+        if (s == 0)
+          mfma_s_first(sacc, kf, qv);
+        else if (s == DL / 16 + DR / 16 - 1)
+          mfma_s_last(sacc, kf, qv);
+        else
+          mfma_s(sacc, kf, qv);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
     // ---- mask + online softmax.  sacc[4 jj + i] is key 8 jj + 4 g + i of row lr ----
-    // scores to log2 units, masked keys to -inf (in place)
+    float sc[16];
     if (t < n_pt) {
       const int count = (int)min<int64_t>(L - (int64_t)t * KT, KT);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = 8 * (e >> 2) + 4 * g + (e & 3);
-        sacc[e] = key < count ? sacc[e] * c_log2 : -INFINITY;
+        sc[e] = key < count ? sacc[e] * c_log2 : -INFINITY;
       }
     } else {
       const uint32_t word = s_mask[row_local][t - n_pt] >> (4 * g);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = 8 * (e >> 2) + (e & 3);          // + 4 g, folded into the shift above
-        sacc[e] = ((word >> key) & 1u) ? sacc[e] * c_log2 : -INFINITY;
+        sc[e] = ((word >> key) & 1u) ? sacc[e] * c_log2 : -INFINITY;
       }
     }
-    float mx = sacc[0];
+    float mx = sc[0];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const bool need = m_new > m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      m_run = need ? m_new : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DL / 32; ++db) oacc[db] *= alpha;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    mx = halves_max(mx);
+    m_max = fmaxf(m_max, mx);
+    if (m_ref == -INFINITY) m_ref = mx;            // first visible keys fix the row's reference
+    overflow |= mx > m_ref + kHeadroomLog2;
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     bf16x8 pb[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sacc[e] - m_use);
+      const float p = __builtin_amdgcn_exp2f(sc[e] - m_use);
       l_run += p;
       pb[e >> 3][e & 7] = (__bf16)p;
     }
 
-    // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row] (fragment reads one step ahead) ----
+    // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row]; V^T reads VRING steps ahead ----
     {
-      bf16x8 vnext = load_vt(buf, voff, 0, 0);
+      constexpr int NST = 2 * (DL / 32);
+      bf16x8 vring[VRING];
 #pragma unroll
-      for (int st = 0; st < 2 * (DL / 32); ++st) {
+      for (int st = 0; st < VRING; ++st) vring[st] = load_vt(buf, voff, st / (DL / 32), st % (DL / 32));
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
         const int ks = st / (DL / 32), db = st % (DL / 32);
-        const bf16x8 vf = vnext;
-        if (st + 1 < 2 * (DL / 32)) vnext = load_vt(buf, voff, (st + 1) / (DL / 32), (st + 1) % (DL / 32));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], oacc[db], 0, 0, 0);
+        const bf16x8 vf = vring[st % VRING];
+        if (st + VRING < NST) vring[st % VRING] = load_vt(buf, voff, (st + VRING) / (DL / 32), (st + VRING) % (DL / 32));
+        if (st == 0)
+          mfma_o_first(oacc[db], vf, pb[ks]);
+        else if (st == NST - 1)
+          mfma_o_last(oacc[db], vf, pb[ks]);
+        else
+          mfma_o(oacc[db], vf, pb[ks]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
+
+  // rare: a score beyond the headroom anywhere in the workgroup -> one more pass
+  if (!__syncthreads_or(overflow ? 1 : 0)) break;
+  m_ref = m_max;
+  }
+
   // ---- epilogue ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = halves_sum(l_run);
   if (!row_ok) return;
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+  const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
   float* orow;
   float* lrow;
   if (a.splits == 1) {

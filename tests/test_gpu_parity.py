@@ -210,3 +210,27 @@ def test_attn_bf16_split_invariance_and_determinism():
         torch.cuda.synchronize()
         assert torch.equal(o, o2) and torch.equal(lse, lse2)
         compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+
+
+def _bf16_bits(x):
+    from synth import bf16_bits
+    return bf16_bits(np.asarray(x, np.float32))
+
+
+@pytest.mark.parametrize("jump_key", [5, 900, 2047])
+def test_attn_bf16_large_score_jump(jump_key):
+    """A key whose score exceeds the first tile's maximum by far more than the kernel's
+    headroom (2^100 in exp2 units) forces the workgroup's second pass."""
+    params = dict(K2)
+    params.update(B=1, N=12, prefix=("fixed", 2048), tree=("bounded", 6, 3))
+    w = make_workload(seed=21, **params)
+    # rotary query of every node/head and rotary key of one prefix row set to 8: that key's
+    # score is 8 * 8 * 64 * scale ~ 296 (natural units), about 427 in log2 units
+    w.q_rope[...] = _bf16_bits(np.full(w.q_rope.shape, 8.0))
+    w.kv[jump_key, w.Dl:] = _bf16_bits(np.full(w.Dr, 8.0))
+    dw = DevWorkload(w)
+    mask, m_ref = check_mask(dw)
+    for s in (1, 3):
+        o, lse = dw.attn(mask, num_splits=s)
+        torch.cuda.synchronize()
+        compare_attn(w, o, lse, *oracle_attn(w, m_ref))
