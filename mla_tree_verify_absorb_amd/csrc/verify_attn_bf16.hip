@@ -70,11 +70,17 @@ constexpr float kHeadroomLog2 = 100.0f;     // scores may exceed a row's referen
 static_assert(KT * R_ROW == NWAVES * 1024, "rotary region must split into one 1 KB load per wave");
 static_assert(LOADS_PER_WAVE == 9, "the tile loop's vmcnt wait assumes 9 loads per wave per tile");
 
-// 16-byte-chunk swizzle of a key row in LDS (XOR of the chunk index's low 3
-// bits).  Key-fragment reads take 8 keys at one chunk; transpose reads take 4
-// consecutive keys x 2 adjacent chunks.  Rows are multiples of 128 bytes, so
-// with 32 banks x 4 bytes both patterns touch distinct bank groups.
-__device__ __forceinline__ int swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+// LDS layout of a tile.  Latent rows: key k at k * 1024, its 16-byte chunk p at
+// 16 * (p >> 4) + ((p & 15) ^ swz(k)).  gfx950 serves 16-byte reads from 64
+// banks, 16 lanes at a time: the key-fragment read (16 consecutive keys, one
+// chunk) needs swz to be a bijection on k & 15, and the transpose read (4
+// consecutive keys, 2 adjacent chunks) needs (swz(k) >> 1) distinct over the 4
+// keys; swz(k) = ((k & 7) << 1) | ((k >> 3) & 1) does both.  The rotary rows
+// (8 chunks) are stored in pairs: keys 2 j and 2 j + 1 share the 256-byte row j,
+// logical chunk (k & 1) * 8 + c at ((k & 1) * 8 + c) ^ (j & 7), which again
+// spreads 16 consecutive keys over all 64 banks.
+__device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+__device__ __forceinline__ int pair_chunk(int key, int c) { return (((key & 1) << 3) | c) ^ ((key >> 1) & 7); }
 
 struct TileSrc {
   const uint16_t* c;   // latent rows of the tile's first key
@@ -128,43 +134,41 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
 }
 
-// Issue this wave's direct-to-LDS 16-byte loads of one tile.  LDS tile layout:
-// latent rows [32][1024 B] then rotary rows [32][128 B]; 16-byte chunk p of a
-// row sits at physical chunk p ^ swz(key).  Wave w loads latent rows
-// w, w + 4, ..., w + 28 (one 64-lane load each: lane = physical chunk, so
-// the lane's global chunk is lane ^ swz(key)), and 1 KB of the rotary region
-// (keys 8 w .. 8 w + 7, lane = key * 8 + physical chunk).  Keys past the
-// tile's valid count re-read its last valid row (masked later).
+// Issue this wave's direct-to-LDS 16-byte loads of one tile (layout above).
+// Wave w loads latent rows w, w + 4, ..., w + 28 (one 64-lane load each; lane =
+// physical chunk, so the lane fetches global chunk lane ^ swz(key)), and the
+// 1 KB of the rotary region holding keys 8 w .. 8 w + 7 (pair rows 4 w ..
+// 4 w + 3; lane = 16 * pair row + physical chunk).  Keys past the tile's valid
+// count re-read its last valid row (masked later).
 __device__ __forceinline__ void issue_tile_loads(const TileSrc& s, uint32_t lds_buf, int wave, int lane) {
-  // keys w + 4 i have swz = 2 w + (i & 1)
-  const uint32_t cb0 = (uint32_t)(lane ^ (2 * wave)) * 16u;
 #pragma unroll
   for (int i = 0; i < C_LOADS_PER_WAVE; ++i) {
     const int key = wave + NWAVES * i;                    // wave-uniform
     const int kc = min(key, s.count - 1);
     const uint16_t* row = s.c + (int64_t)kc * s.ldc;      // scalar address
-    lds_dma16(lds_buf + key * C_ROW, row, (i & 1) ? (cb0 ^ 16u) : cb0);
+    lds_dma16(lds_buf + key * C_ROW, row, (uint32_t)(lane ^ swz(key)) * 16u);
   }
   {
-    const int key = wave * 8 + (lane >> 3);
+    const int pr = wave * 4 + (lane >> 4);                // pair row
+    const int logical = (lane & 15) ^ (pr & 7);
+    const int key = 2 * pr + (logical >> 3);
     const int kc = min(key, s.count - 1);
-    const int p = (lane & 7) ^ swz(key);
-    lds_dma16(lds_buf + R_OFF + wave * 1024, s.r, (uint32_t)(kc * s.ldr + p * 8) * 2u);
+    lds_dma16(lds_buf + R_OFF + wave * 1024, s.r, (uint32_t)(kc * s.ldr + (logical & 7) * 8) * 2u);
   }
 }
 
-// Byte offset in a tile of the K fragment for latent k-step s (< 32).
-__device__ __forceinline__ int kaddr(int kbase, int ksw, int s) {
-  return kbase + (s >> 2) * 128 + (((2 * (s & 3)) ^ ksw) << 4);
-}
+// Byte offset in a tile of the K fragment for latent k-step s (< 32): key lr,
+// logical chunk 2 s + g; kbase = lr * 1024 + ((g ^ swz(lr)) << 4).
+__device__ __forceinline__ int kaddr(int kbase, int s) { return (kbase ^ ((s & 7) << 5)) + (s >> 3) * 256; }
 
 // V^T fragment of 16-key step ks and 32-dim block db: two transpose reads of
-// 4 keys each (keys 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3).  An odd db
-// sets bit 2 of the logical chunk, i.e. flips bit 6 of the byte offset.
+// 4 keys each (keys 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3).  voff holds
+// the lane's row and swizzled chunk for db = 0, first read; db & 3 and the +8
+// keys (whose swizzle differs in bit 0) enter by XOR, db >> 2 and ks by offset.
 __device__ __forceinline__ bf16x8 load_vt(const unsigned char* buf, int voff, int ks, int db) {
-  const unsigned char* va = buf + ((db & 1) ? (voff ^ 64) : voff) + ks * 16 * C_ROW + (db >> 1) * 128;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * C_ROW));
+  const int o = (voff ^ ((db & 3) << 6)) + (db >> 2) * 256 + ks * 16 * C_ROW;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + o));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + (o ^ 16) + 8 * C_ROW));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -277,7 +281,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
 
   // ---- query fragments: B operand, lane (lr, g) holds Q[row lr][16 s + 8 g .. +8] ----
   // The 32 latent k-steps stay in VGPRs; the 4 rotary k-steps are staged in LDS
-  // (row rl, 16-byte chunk p at p ^ (rl & 7)) and read per tile.
+  // in the rotary pair-row layout (row rl at pair row rl >> 1) and read per tile.
   const int r_loc = rb * ROWS + wave * 32 + lr;
   const bool row_ok = r_loc < n_rows;
   const int64_t grow = (int64_t)b * n_rows + (row_ok ? r_loc : 0);
@@ -295,29 +299,24 @@ verify_attn_bf16_kernel(AttnArgs a) {
     for (int c = g; c < DR / 8; c += 2) {
       const bf16x8 v0 = qr[c];
       const bf16x8 v = row_ok ? v0 : bf16x8{};
-      *reinterpret_cast<bf16x8*>(s_qr + row_local * R_ROW + ((c ^ (row_local & 7)) << 4)) = v;
+      *reinterpret_cast<bf16x8*>(s_qr + (row_local >> 1) * 256 + (pair_chunk(row_local, c) << 4)) = v;
     }
   }
 
   // ---- LDS addresses (lane constants) ----
-  // K fragment (A of S^T): key lr, logical chunk 2 s + g.  With s = 4 a + s',
-  // the swizzled chunk is 8 a + ((2 s' + g) ^ swz(lr)); the rotary steps
-  // (s >= 32) read the rotary row of key lr the same way.
-  const int kbase = lr * C_ROW;
-  const int ksw = g ^ swz(lr);              // (2 s' + g) ^ swz(lr) = 2 s' ^ ksw
+  const int kbase = lr * C_ROW + ((g ^ swz(lr)) << 4);   // K fragment, k-step 0
   // V^T fragment (A of O^T) by transpose read.  Lane = 16 G + 4 rr + cc reads key
-  // 16 ks + 4 g + rr (+8 for the second read), dims 32 db + 16 (G & 1) + 4 cc .. +3.
+  // 16 ks + 4 g + rr (+8 for the second read), dims 32 db + 16 (G & 1) + 4 cc .. +3,
+  // i.e. logical chunk 4 db + 2 (G & 1) + (cc >> 1), byte 8 (cc & 1) in it.
   int voff;
   {
     const int G = lane >> 4;
     const int rr = (lane >> 2) & 3;
     const int cc = lane & 3;
-    const int vkey = 4 * g + rr;            // key within a 16-key step (low 3 bits fix the swizzle)
-    const int pl = 2 * (G & 1) + (cc >> 1); // low 3 bits of the logical chunk for even db
-    voff = vkey * C_ROW + ((pl ^ swz(vkey)) << 4) + (cc & 1) * 8;   // odd db: chunk bit 2 flips
+    const int vkey = 4 * g + rr;
+    voff = vkey * C_ROW + (((2 * (G & 1) + (cc >> 1)) ^ swz(vkey)) << 4) + (cc & 1) * 8;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)s_kv;   // LDS byte address of the ring
-  const unsigned char* qr_row = s_qr + row_local * R_ROW;
 
   // ---- accumulators and softmax state (one query row per lane) ----
   // Each row's probabilities are taken relative to a fixed reference m_ref:
@@ -358,18 +357,19 @@ verify_attn_bf16_kernel(AttnArgs a) {
       bf16x8 kring[KRING];
       bf16x8 qrr[DR / 16];
 #pragma unroll
-      for (int s = 0; s < KRING; ++s) kring[s] = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, s));
+      for (int s = 0; s < KRING; ++s) kring[s] = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, s));
 #pragma unroll
       for (int s = 0; s < DL / 16 + DR / 16; ++s) {
         const bf16x8 kf = kring[s % KRING];
         const int nx = s + KRING;
         if (nx < DL / 16) {
-          kring[s % KRING] = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, ksw, nx));
+          kring[s % KRING] = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, nx));
         } else if (nx < DL / 16 + DR / 16) {
           // rotary steps: key rows from the tile's rotary region, queries from s_qr
           const int c = 2 * (nx - DL / 16) + g;
-          kring[s % KRING] = *reinterpret_cast<const bf16x8*>(buf + R_OFF + lr * R_ROW + ((c ^ swz(lr)) << 4));
-          qrr[nx - DL / 16] = *reinterpret_cast<const bf16x8*>(qr_row + ((c ^ (row_local & 7)) << 4));
+          kring[s % KRING] = *reinterpret_cast<const bf16x8*>(buf + R_OFF + (lr >> 1) * 256 + (pair_chunk(lr, c) << 4));
+          qrr[nx - DL / 16] =
+              *reinterpret_cast<const bf16x8*>(s_qr + (row_local >> 1) * 256 + (pair_chunk(row_local, c) << 4));
         }
         const bf16x8 qv = s < DL / 16 ? qf[s] : qrr[s - DL / 16];
         if (s == 0)
