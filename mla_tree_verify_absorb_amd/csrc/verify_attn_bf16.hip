@@ -14,8 +14,9 @@
 //  * All H heads of all N tree nodes of a request read the same latent KV
 //    stream, so (node, head) pairs are the rows of a dense contraction.  A
 //    workgroup of 4 waves owns 128 rows; each wave 32 rows.
-//  * The 32 rows' absorbed queries stay in VGPRs for the whole kernel (36
-//    bf16x8 B-fragments, 144 VGPRs).
+//  * The 32 rows' absorbed queries stay in VGPRs for the whole kernel (28
+//    bf16x8 B-fragments, 112 VGPRs); the last 4 latent and the 4 rotary
+//    k-steps are staged in LDS and read per tile.
 //  * KV tiles of 32 keys x 576 bf16 are copied HBM -> LDS with direct-to-LDS
 //    16-byte loads into a 3-deep ring, with a 16-byte-chunk XOR swizzle that
 //    keeps both read patterns below bank-conflict free.
@@ -31,6 +32,10 @@
 //    (the first visible tile's max, with 2^100 of headroom), so the
 //    accumulators are never rescaled; a score beyond the headroom triggers
 //    one rerun of the workgroup's tiles with the true row maximum.
+//  * Software pipeline: iteration t runs the S^T MFMAs of tile t + 1, then
+//    the O^T MFMAs of tile t, and computes the probabilities of tile t + 1
+//    (one element per MFMA) in the shadow of the latter, so no softmax work
+//    sits between the two MFMA streams on the common path.
 //  * MFMAs are issued by inline asm to pin S^T to VGPRs and O^T to AGPRs;
 //    LDS fragment reads run 4 MFMAs ahead; workgroups are mapped so that a
 //    request's row blocks share one XCD's L2.
@@ -81,6 +86,12 @@ static_assert(LOADS_PER_WAVE == 9, "the tile loop's vmcnt wait assumes 9 loads p
 // spreads 16 consecutive keys over all 64 banks.
 __device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
 __device__ __forceinline__ int pair_chunk(int key, int c) { return (((key & 1) << 3) | c) ^ ((key >> 1) & 7); }
+
+// Hides a value from the optimiser (no code is emitted).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 struct TileSrc {
   const uint16_t* c;   // latent rows of the tile's first key
@@ -146,10 +157,12 @@ __device__ __forceinline__ void issue_tile_loads(const TileSrc& s, uint32_t lds_
     const int key = wave + NWAVES * i;                    // wave-uniform
     const int kc = min(key, s.count - 1);
     const uint16_t* row = s.c + (int64_t)kc * s.ldc;      // scalar address
-    lds_dma16(lds_buf + key * C_ROW, row, (uint32_t)(lane ^ swz(key)) * 16u);
+    // lane offsets are recomputed per copy (opaque to the optimiser) instead of
+    // being kept in, or spilled from, registers across the tile loop
+    lds_dma16(lds_buf + key * C_ROW, row, (uint32_t)(opaque(lane << 4) ^ (swz(key) << 4)));
   }
   {
-    const int pr = wave * 4 + (lane >> 4);                // pair row
+    const int pr = wave * 4 + (opaque(lane) >> 4);        // pair row
     const int logical = (lane & 15) ^ (pr & 7);
     const int key = 2 * pr + (logical >> 3);
     const int kc = min(key, s.count - 1);
@@ -178,9 +191,9 @@ __device__ __forceinline__ bf16x8 load_vt(const unsigned char* buf, int voff, in
 // the 512 x 32 output accumulator in AGPRs.  The compiler does not model the
 // MFMA pipeline behind an asm statement, so the wait states it would insert
 // are written out: 16 after the last S^T MFMA of a tile before VALU reads of
-// S^T, 16 after the last O^T MFMA of a tile before any AGPR read, and 4
-// between the VALU writes of P (and of rescaled AGPRs) and the first O^T
-// MFMA.  Chained MFMAs on one accumulator need no wait states.
+// S^T, 16 after the tile loop before any AGPR read or rewrite, and 4 between
+// VALU writes of P and the first O^T MFMA of a tile.  Chained MFMAs on one
+// accumulator need no wait states.
 __device__ __forceinline__ void mfma_s_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
@@ -202,14 +215,6 @@ __device__ __forceinline__ void mfma_o_first(f32x16& acc, const bf16x8& a, const
   asm volatile(
       "s_nop 3\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-      : "+a"(acc)
-      : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_o_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile(
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7"
       : "+a"(acc)
       : "v"(a), "v"(b));
 }
@@ -236,13 +241,16 @@ __device__ __forceinline__ int xcd_local_item(int block, int total) {
 }
 
 constexpr int KRING = 4;   // K-fragment reads in flight ahead of the S^T MFMAs
+constexpr int QREG = DL / 16 - 4;   // latent query k-steps held in VGPRs; the last 4 are staged in LDS
+static_assert(DL / 16 - QREG == DR / 16, "the staged latent queries use the rotary pair-row layout");
 constexpr int VRING = 4;   // V^T-fragment reads in flight ahead of the O^T MFMAs
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 verify_attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char s_kv[NBUF * TILE_BYTES];
   __shared__ uint32_t s_mask[ROWS][MAXW];
-  __shared__ __attribute__((aligned(16))) unsigned char s_qr[ROWS * R_ROW];   // rotary queries, swizzled rows
+  // queries of the last QREG_LDS latent k-steps (part 0) and the rotary ones (part 1), swizzled pair rows
+  __shared__ __attribute__((aligned(16))) unsigned char s_qx[2 * ROWS * R_ROW];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -286,20 +294,24 @@ verify_attn_bf16_kernel(AttnArgs a) {
   const bool row_ok = r_loc < n_rows;
   const int64_t grow = (int64_t)b * n_rows + (row_ok ? r_loc : 0);
   const int row_local = wave * 32 + lr;
-  bf16x8 qf[DL / 16];
+  bf16x8 qf[QREG];
   {
     const bf16x8* ql = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q_lat) + grow * DL) + g;
 #pragma unroll
     for (int s = 0; s < DL / 16; ++s) {
-      const bf16x8 v = ql[2 * s];
-      qf[s] = row_ok ? v : bf16x8{};
+      const bf16x8 v0 = ql[2 * s];
+      const bf16x8 v = row_ok ? v0 : bf16x8{};
+      if (s < QREG)
+        qf[s] = v;
+      else
+        *reinterpret_cast<bf16x8*>(s_qx + (row_local >> 1) * 256 + (pair_chunk(row_local, 2 * (s - QREG) + g) << 4)) = v;
     }
     const bf16x8* qr = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q_rope) + grow * DR);
 #pragma unroll
     for (int c = g; c < DR / 8; c += 2) {
       const bf16x8 v0 = qr[c];
       const bf16x8 v = row_ok ? v0 : bf16x8{};
-      *reinterpret_cast<bf16x8*>(s_qr + (row_local >> 1) * 256 + (pair_chunk(row_local, c) << 4)) = v;
+      *reinterpret_cast<bf16x8*>(s_qx + ROWS * R_ROW + (row_local >> 1) * 256 + (pair_chunk(row_local, c) << 4)) = v;
     }
   }
 
@@ -333,90 +345,140 @@ verify_attn_bf16_kernel(AttnArgs a) {
   float l_run = 0.f;         // this lane's half of the row's exp-sum
   const float c_log2 = a.scale * 1.4426950408889634f;
 
+  // Ring slot 2 starts zeroed: the first PV of a pass runs on it with a zero P.
+  for (int i = tid; i < TILE_BYTES / 16; i += 256)
+    reinterpret_cast<uint4*>(s_kv + 2 * TILE_BYTES)[i] = make_uint4(0u, 0u, 0u, 0u);
+
   for (int pass = 0; pass < 2; ++pass) {
   bool overflow = false;
   l_run = 0.f;
 #pragma unroll
   for (int db = 0; db < DL / 32; ++db) oacc[db] = f32x16{};
 
-  // ---- prologue: first two tiles in flight ----
+  // Software pipeline: iteration t runs QK of tile t + 1, then PV of tile t, and
+  // computes P of tile t + 1 in the shadow of the PV MFMAs.  Tile t + 1 lives in
+  // ring slot (j + 1) % 3, tile t in j % 3; the copies of tile t + 2 go to slot
+  // (j + 2) % 3, whose last reader (PV of tile t - 1) every wave has finished
+  // by the barrier at the top of iteration t.
+
+  // ---- prologue: tile t0 in flight ----
+  bf16x8 pb[2] = {bf16x8{}, bf16x8{}};
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing of the compiler's pending inside the loop
   if (t0 < t1) issue_tile_loads(tile_source(a, b, p0, L, n_pt, t0), lds0, wave, lane);
-  if (t0 + 1 < t1) issue_tile_loads(tile_source(a, b, p0, L, n_pt, t0 + 1), lds0 + TILE_BYTES, wave, lane);
+  int slot = 2;                          // ring slot of tile t (t0 - 1: none)
 
-  for (int t = t0; t < t1; ++t) {
-    const int j = t - t0;
-    const unsigned char* buf = s_kv + (j % NBUF) * TILE_BYTES;
-    wait_vmcnt_le(t + 1 < t1 ? LOADS_PER_WAVE : 0);   // this wave's loads of tile t are done
-    __syncthreads();   // tile t visible to all waves; every wave is done with tile t-1
-    if (t + 2 < t1) issue_tile_loads(tile_source(a, b, p0, L, n_pt, t + 2), lds0 + ((j + 2) % NBUF) * TILE_BYTES,
-                                     wave, lane);
+  for (int t = t0 - 1; t < t1; ++t) {
+    const int slot_n = slot == 2 ? 0 : slot + 1;      // tile t + 1
+    const int slot_d = slot_n == 2 ? 0 : slot_n + 1;  // tile t + 2
+    const int tn = t + 1;
+    f32x16 sn;                    // S^T, then exponents, of tile tn
+    float c, m, m_abs;
+    if (tn < t1) {
+      wait_vmcnt_le(0);           // this wave's copies of tile tn have landed
+      __syncthreads();            // ... and every wave's; every wave is done with tile t - 1
 
-    // ---- S^T[key][row] = K . Q^T over 576 dims; K-fragment reads KRING steps ahead ----
-    f32x16 sacc;
-    {
-      bf16x8 kring[KRING];
-      bf16x8 qrr[DR / 16];
+      // ---- S^T[key][row] = K . Q^T over 576 dims for tile tn; K-fragment reads
+      // KRING steps ahead, rotary query fragments QRING ahead.  The copies of tile
+      // tn + 1 are issued once the first fragment reads are in flight. ----
+      {
+        const unsigned char* kbuf = s_kv + slot_n * TILE_BYTES;
+        constexpr int QRING = 2;
+        bf16x8 kring[KRING];
+        bf16x8 qrr[QRING];
 #pragma unroll
-      for (int s = 0; s < KRING; ++s) kring[s] = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, s));
+        for (int s = 0; s < KRING; ++s) kring[s] = *reinterpret_cast<const bf16x8*>(kbuf + kaddr(kbase, s));
+        if (tn + 1 < t1)
+          issue_tile_loads(tile_source(a, b, p0, L, n_pt, tn + 1), lds0 + slot_d * TILE_BYTES, wave, lane);
 #pragma unroll
-      for (int s = 0; s < DL / 16 + DR / 16; ++s) {
-        const bf16x8 kf = kring[s % KRING];
-        const int nx = s + KRING;
-        if (nx < DL / 16) {
-          kring[s % KRING] = *reinterpret_cast<const bf16x8*>(buf + kaddr(kbase, nx));
-        } else if (nx < DL / 16 + DR / 16) {
-          // rotary steps: key rows from the tile's rotary region, queries from s_qr
-          const int c = 2 * (nx - DL / 16) + g;
-          kring[s % KRING] = *reinterpret_cast<const bf16x8*>(buf + R_OFF + (lr >> 1) * 256 + (pair_chunk(lr, c) << 4));
-          qrr[nx - DL / 16] =
-              *reinterpret_cast<const bf16x8*>(s_qr + (row_local >> 1) * 256 + (pair_chunk(row_local, c) << 4));
+        for (int s = 0; s < DL / 16 + DR / 16; ++s) {
+          const bf16x8 kf = kring[s % KRING];
+          const int nx = s + KRING;
+          if (nx < DL / 16) {
+            kring[s % KRING] = *reinterpret_cast<const bf16x8*>(kbuf + kaddr(kbase, nx));
+          } else if (nx < DL / 16 + DR / 16) {   // rotary key rows
+            const int cc = 2 * (nx - DL / 16) + g;
+            kring[s % KRING] =
+                *reinterpret_cast<const bf16x8*>(kbuf + R_OFF + (lr >> 1) * 256 + (pair_chunk(lr, cc) << 4));
+          }
+          const bf16x8 qv = s < QREG ? qf[s] : qrr[s % QRING];
+          const int nq = s + QRING;
+          if (nq >= QREG && nq < DL / 16 + DR / 16) {   // queries staged in s_qx
+            const int part = nq >= DL / 16;
+            const int cc = 2 * (part ? nq - DL / 16 : nq - QREG) + g;
+            qrr[nq % QRING] = *reinterpret_cast<const bf16x8*>(s_qx + part * ROWS * R_ROW + (row_local >> 1) * 256 +
+                                                               (pair_chunk(row_local, cc) << 4));
+          }
+          if (s == 0)
+            mfma_s_first(sn, kf, qv);
+          else if (s == DL / 16 + DR / 16 - 1)
+            mfma_s_last(sn, kf, qv);
+          else
+            mfma_s(sn, kf, qv);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        const bf16x8 qv = s < DL / 16 ? qf[s] : qrr[s - DL / 16];
-        if (s == 0)
-          mfma_s_first(sacc, kf, qv);
-        else if (s == DL / 16 + DR / 16 - 1)
-          mfma_s_last(sacc, kf, qv);
-        else
-          mfma_s(sacc, kf, qv);
-        __builtin_amdgcn_sched_barrier(0);
       }
-    }
 
-    // ---- mask + online softmax.  sacc[4 jj + i] is key 8 jj + 4 g + i of row lr ----
-    float sc[16];
-    if (t < n_pt) {
-      const int count = (int)min<int64_t>(L - (int64_t)t * KT, KT);
+      // ---- scores -> exponent form.  sn[4 jj + i] is key 8 jj + 4 g + i of row lr.
+      // P element e is 2^(c * sn[e] - m).  Full prefix tiles, once every row has its
+      // reference, use (c, m) = (scale * log2 e, m_ref) directly.  Other tiles (the
+      // partial last prefix tile, tree tiles, a row's first visible tile) are masked
+      // here: sn becomes the masked exponent itself and (c, m) = (1, 0), and a row's
+      // first visible tile fixes its reference.  m_abs is the absolute value (log2
+      // units) the exponents are relative to. ----
+      const bool fast = tn < n_pt && (int64_t)(tn + 1) * KT <= L &&
+                        __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) == 0;
+      if (fast) {
+        c = c_log2;
+        m = m_ref;
+        m_abs = m_ref;
+      } else {
+        float sc[16];
+        if (tn < n_pt) {
+          const int count = (int)min<int64_t>(L - (int64_t)tn * KT, KT);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = 8 * (e >> 2) + 4 * g + (e & 3);
-        sc[e] = key < count ? sacc[e] * c_log2 : -INFINITY;
+          for (int e = 0; e < 16; ++e) {
+            const int key = 8 * (e >> 2) + 4 * g + (e & 3);
+            sc[e] = key < count ? sn[e] * c_log2 : -INFINITY;
+          }
+        } else {
+          // the row offset is recomputed here (opaque to the optimiser) rather
+          // than carried round the loop in a register
+          const int mrow = opaque(row_local * MAXW);
+          const uint32_t word = (&s_mask[0][0])[mrow + (tn - n_pt)] >> (4 * g);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = 8 * (e >> 2) + (e & 3);          // + 4 g, folded into the shift above
+            sc[e] = ((word >> key) & 1u) ? sn[e] * c_log2 : -INFINITY;
+          }
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+        mx = halves_max(mx);
+        if (m_ref == -INFINITY) m_ref = mx;            // first visible keys fix the row's reference
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sn[e] = sc[e] - m_use;
+        c = 1.f;
+        m = 0.f;
+        m_abs = m_use;
       }
     } else {
-      const uint32_t word = s_mask[row_local][t - n_pt] >> (4 * g);
+      // nothing after this tile: the shadow work below evaluates to p = 0
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = 8 * (e >> 2) + (e & 3);          // + 4 g, folded into the shift above
-        sc[e] = ((word >> key) & 1u) ? sacc[e] * c_log2 : -INFINITY;
-      }
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
-    mx = halves_max(mx);
-    m_max = fmaxf(m_max, mx);
-    if (m_ref == -INFINITY) m_ref = mx;            // first visible keys fix the row's reference
-    overflow |= mx > m_ref + kHeadroomLog2;
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sc[e] - m_use);
-      l_run += p;
-      pb[e >> 3][e & 7] = (__bf16)p;
+      for (int e = 0; e < 16; ++e) sn[e] = 0.f;
+      c = 0.f;
+      m = INFINITY;
+      m_abs = 0.f;
     }
 
-    // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row]; V^T reads VRING steps ahead ----
+    // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row] for tile t (the pass's first
+    // iteration multiplies a zero P with the zero-filled slot 2); V^T reads VRING steps
+    // ahead.  P of tile tn (one element per MFMA), then its row max, in the shadow. ----
+    bf16x8 pn[2];
+    float mx = -INFINITY;
     {
+      const unsigned char* buf = s_kv + slot * TILE_BYTES;
       constexpr int NST = 2 * (DL / 32);
       bf16x8 vring[VRING];
 #pragma unroll
@@ -428,15 +490,27 @@ verify_attn_bf16_kernel(AttnArgs a) {
         if (st + VRING < NST) vring[st % VRING] = load_vt(buf, voff, (st + VRING) / (DL / 32), (st + VRING) % (DL / 32));
         if (st == 0)
           mfma_o_first(oacc[db], vf, pb[ks]);
-        else if (st == NST - 1)
-          mfma_o_last(oacc[db], vf, pb[ks]);
         else
           mfma_o(oacc[db], vf, pb[ks]);
+        if (st < 16) {
+          const float x = __builtin_fmaf(sn[st], c, -m);
+          mx = fmaxf(mx, x);
+          const float pe = __builtin_amdgcn_exp2f(x);
+          l_run += pe;
+          pn[st >> 3][st & 7] = (__bf16)pe;
+        } else if (st == 16) {
+          mx = halves_max(mx);
+          m_max = fmaxf(m_max, m_abs + mx);
+          overflow |= mx > kHeadroomLog2;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    pb[0] = pn[0];
+    pb[1] = pn[1];
+    slot = slot_n;
   }
-
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");   // last O^T MFMA -> AGPR reads / rewrites
 
   // rare: a score beyond the headroom anywhere in the workgroup -> one more pass
   if (!__syncthreads_or(overflow ? 1 : 0)) break;
