@@ -121,7 +121,8 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *                    ddtree_verify_attn_workspace_size(...) with the same shape
  *                    and num_splits (may be NULL when that size is 0)
  * bf16 inputs need 16-byte aligned base pointers and row strides that are
- * multiples of 8 elements.  Requests whose tree_ok is 0 give undefined o/lse.
+ * multiples of 8 elements (INVALID_ARG otherwise) and at most 2^24 elements
+ * (UNSUPPORTED otherwise).  Requests whose tree_ok is 0 give undefined o/lse.
  */
 size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                          int64_t max_prefix_len, int32_t num_splits);

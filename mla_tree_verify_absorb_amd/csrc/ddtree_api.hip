@@ -140,6 +140,10 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
         !aligned16(krope_tree) || !aligned16(o))
       return DDTREE_ERR_INVALID_ARG;
     if ((ld_ckv | ld_krope | ld_ckv_tree | ld_krope_tree) & 7) return DDTREE_ERR_INVALID_ARG;
+    // the kernel forms byte offsets of a 32-key tile's rows in 32 bits
+    if (ld_ckv > kMaxBf16RowStride || ld_krope > kMaxBf16RowStride || ld_ckv_tree > kMaxBf16RowStride ||
+        ld_krope_tree > kMaxBf16RowStride)
+      return DDTREE_ERR_UNSUPPORTED;
   }
   // ---- workspace ----
   const int splits = resolve_splits(dtype, B, N, H, max_prefix_len, num_splits);

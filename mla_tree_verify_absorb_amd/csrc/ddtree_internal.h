@@ -43,6 +43,7 @@ constexpr int kMfmaDl = 512;
 constexpr int kMfmaDr = 64;
 constexpr int kRowsPerBlock = 128;   // query rows (node, head) per workgroup
 constexpr int kKeysPerTile = 32;     // latent KV rows per LDS tile
+constexpr int64_t kMaxBf16RowStride = int64_t(1) << 24;   // elements; keeps tile row offsets in 32 bits
 
 hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_verify_attn_f32(const AttnArgs& a, hipStream_t stream);

@@ -92,6 +92,10 @@ __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 struct TileSrc {
   const uint16_t* c;   // latent rows of the tile's first key
@@ -167,6 +171,61 @@ __device__ __forceinline__ void issue_tile_loads(const TileSrc& s, uint32_t lds_
     const int key = 2 * pr + (logical >> 3);
     const int kc = min(key, s.count - 1);
     lds_dma16(lds_buf + R_OFF + wave * 1024, s.r, (uint32_t)(kc * s.ldr + (logical & 7) * 8) * 2u);
+  }
+}
+
+// Copies of one tile spread through the S^T MFMA stream.  A CopyPlan holds the
+// tile's row bases and strides (scalar) and its valid key count; copy i < 8
+// loads latent key wave + 4 i (clamped to the last valid key), copy 8 the
+// wave's 1 KB of rotary pair rows, in the LDS layout of issue_tile_loads.  The
+// swizzle of key wave + 4 i is 2 wave + 8 (i & 1) + ((i >> 1) & 1), so the
+// lane's chunk offset (lane ^ swz) * 16 is lw[i & 1] ^ (16 if i & 2) with
+// lw0 = 16 lane ^ 32 wave and lw1 = lw0 ^ 128.  The rotary copy of lane
+// (pair row 4 wave + lane / 16) reads key rkey (clamped), 16-byte piece rpiece.
+struct CopyLanes {
+  uint32_t lw0, lw1;   // latent chunk offsets for even / odd i
+  int rkey;            // rotary: the lane's key within the tile
+  uint32_t rpiece;     // rotary: byte offset of the lane's 16 bytes within the key's rotary row
+};
+struct CopyPlan {
+  const unsigned char* c;   // latent row of the tile's first key
+  const unsigned char* r;   // rotary row of the tile's first key
+  uint32_t cstride, rstride;  // row strides in bytes
+  int count;                // valid keys (1..32)
+};
+
+__device__ __forceinline__ CopyPlan copy_plan(const AttnArgs& a, int b, int64_t p0, int64_t L, int n_pt, int t) {
+  CopyPlan q;
+  if (t < n_pt) {
+    const int64_t row0 = p0 + (int64_t)t * KT;
+    q.c = static_cast<const unsigned char*>(a.ckv) + row0 * a.ld_ckv * 2;
+    q.r = static_cast<const unsigned char*>(a.krope) + row0 * a.ld_krope * 2;
+    q.cstride = (uint32_t)(a.ld_ckv * 2);
+    q.rstride = (uint32_t)(a.ld_krope * 2);
+    const int64_t rem = L - (int64_t)t * KT;
+    q.count = rem < KT ? (int)rem : KT;
+  } else {
+    const int node0 = (t - n_pt) * KT;
+    const int64_t row0 = (int64_t)b * a.N + node0;
+    q.c = static_cast<const unsigned char*>(a.ckv_tree) + row0 * a.ld_ckv_tree * 2;
+    q.r = static_cast<const unsigned char*>(a.krope_tree) + row0 * a.ld_krope_tree * 2;
+    q.cstride = (uint32_t)(a.ld_ckv_tree * 2);
+    q.rstride = (uint32_t)(a.ld_krope_tree * 2);
+    const int rem = a.N - node0;
+    q.count = rem < KT ? rem : KT;
+  }
+  return q;
+}
+
+__device__ __forceinline__ void issue_copy(const CopyPlan& q, const CopyLanes& cl, uint32_t lds_buf, int wave, int i) {
+  if (i < C_LOADS_PER_WAVE) {
+    const int key = wave + NWAVES * i;
+    const uint32_t kc = (uint32_t)min(key, q.count - 1);
+    const uint32_t lw = (i & 1) ? opaque(cl.lw1) : opaque(cl.lw0);
+    lds_dma16(lds_buf + key * C_ROW, q.c, (lw ^ ((i & 2) ? 16u : 0u)) + kc * q.cstride);
+  } else {
+    const uint32_t kc = (uint32_t)min(opaque(cl.rkey), q.count - 1);
+    lds_dma16(lds_buf + R_OFF + wave * 1024, q.r, kc * q.rstride + opaque(cl.rpiece));
   }
 }
 
@@ -329,6 +388,15 @@ verify_attn_bf16_kernel(AttnArgs a) {
     voff = vkey * C_ROW + (((2 * (G & 1) + (cc >> 1)) ^ swz(vkey)) << 4) + (cc & 1) * 8;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)s_kv;   // LDS byte address of the ring
+  CopyLanes clanes;
+  {
+    clanes.lw0 = (uint32_t)((lane << 4) ^ (wave << 5));
+    clanes.lw1 = clanes.lw0 ^ 128u;
+    const int pr = wave * 4 + (lane >> 4);
+    const int logical = (lane & 15) ^ (pr & 7);
+    clanes.rkey = 2 * pr + (logical >> 3);
+    clanes.rpiece = (uint32_t)((logical & 7) * 16);
+  }
 
   // ---- accumulators and softmax state (one query row per lane) ----
   // Each row's probabilities are taken relative to a fixed reference m_ref:
@@ -387,8 +455,10 @@ verify_attn_bf16_kernel(AttnArgs a) {
         bf16x8 qrr[QRING];
 #pragma unroll
         for (int s = 0; s < KRING; ++s) kring[s] = *reinterpret_cast<const bf16x8*>(kbuf + kaddr(kbase, s));
-        if (tn + 1 < t1)
-          issue_tile_loads(tile_source(a, b, p0, L, n_pt, tn + 1), lds0 + slot_d * TILE_BYTES, wave, lane);
+        // tile tn + 1 (past the end: tile t1 - 1 again, into the free slot, so
+        // that the copies need no branch); one copy every third S^T MFMA
+        const CopyPlan cplan = copy_plan(a, b, p0, L, n_pt, min(tn + 1, t1 - 1));
+        const uint32_t lds_d = lds0 + slot_d * TILE_BYTES;
 #pragma unroll
         for (int s = 0; s < DL / 16 + DR / 16; ++s) {
           const bf16x8 kf = kring[s % KRING];
@@ -408,6 +478,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
             qrr[nq % QRING] = *reinterpret_cast<const bf16x8*>(s_qx + part * ROWS * R_ROW + (row_local >> 1) * 256 +
                                                                (pair_chunk(row_local, cc) << 4));
           }
+          if (s % 3 == 1 && s / 3 < LOADS_PER_WAVE) issue_copy(cplan, clanes, lds_d, wave, s / 3);
           if (s == 0)
             mfma_s_first(sn, kf, qv);
           else if (s == DL / 16 + DR / 16 - 1)
@@ -476,6 +547,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
     // iteration multiplies a zero P with the zero-filled slot 2); V^T reads VRING steps
     // ahead.  P of tile tn (one element per MFMA), then its row max, in the shadow. ----
     bf16x8 pn[2];
+    float pe[16];
     float mx = -INFINITY;
     {
       const unsigned char* buf = s_kv + slot * TILE_BYTES;
@@ -492,14 +564,24 @@ verify_attn_bf16_kernel(AttnArgs a) {
           mfma_o_first(oacc[db], vf, pb[ks]);
         else
           mfma_o(oacc[db], vf, pb[ks]);
-        if (st < 16) {
-          const float x = __builtin_fmaf(sn[st], c, -m);
-          mx = fmaxf(mx, x);
-          const float pe = __builtin_amdgcn_exp2f(x);
-          l_run += pe;
-          pn[st >> 3][st & 7] = (__bf16)pe;
-        } else if (st == 16) {
-          mx = halves_max(mx);
+        // three-stage pipeline over the 16 elements, so that the VALU work of one
+        // step is independent: exponent of element st, 2^x and row max of st - 1,
+        // exp-sum and bf16 pair of st - 2
+        if (st < 16) sn[st] = __builtin_fmaf(sn[st], c, -m);
+        if (st >= 1 && st <= 16) {
+          pe[st - 1] = __builtin_amdgcn_exp2f(sn[st - 1]);
+          mx = fmaxf(mx, sn[st - 1]);
+        }
+        if (st >= 2 && st <= 17) {
+          const int e = st - 2;
+          l_run += pe[e];
+          if (e & 1) {
+            pn[e >> 3][(e - 1) & 7] = (__bf16)pe[e - 1];
+            pn[e >> 3][e & 7] = (__bf16)pe[e];
+          }
+        }
+        if (st == 18) mx = halves_max(mx);
+        if (st == 19) {
           m_max = fmaxf(m_max, m_abs + mx);
           overflow |= mx > kHeadroomLog2;
         }
@@ -511,6 +593,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
     slot = slot_n;
   }
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");   // last O^T MFMA -> AGPR reads / rewrites
+  wait_vmcnt_le(0);   // the repeated copy of the last tile (if any) has landed
 
   // rare: a score beyond the headroom anywhere in the workgroup -> one more pass
   if (!__syncthreads_or(overflow ? 1 : 0)) break;

@@ -98,6 +98,8 @@ def test_verify_attn_rejects_bad_pointers_strides_and_scale():
     assert attn(ld_ckv=500) == INVALID                # row stride shorter than a row
     assert attn(ld_krope=60) == INVALID
     assert attn(ld_ckv=580) == INVALID                # bf16 rows must be 16-byte multiples
+    assert attn(ld_ckv=(1 << 24) + 8) == UNSUPPORTED   # bf16 tile row offsets are 32-bit
+    assert attn(ld_krope_t=(1 << 24) + 8) == UNSUPPORTED
     assert attn(ckv=A + (2 << 24) + 2) == INVALID     # misaligned bf16 base
     assert attn(scale=float("nan")) == INVALID
     assert attn(scale=float("inf")) == INVALID
