@@ -205,3 +205,43 @@ def greedy_accept_ref(logits, tokens, parents):
         committed = [int(tokens[b, k]) for k in best[1:]] + [int(tstar[b, best[-1]])]
         commit[b, :len(committed)] = committed
     return tstar, accept_len, accept_nodes, commit
+
+
+# ----------------------------------------------------------------------------
+# KV-cache compaction after acceptance
+# ----------------------------------------------------------------------------
+
+def compact_kv_ref(ckv_tree, krope_tree, accept_len, accept_nodes, ckv, krope, dest_rows):
+    """Move the accepted path's latent rows into the cache, in place.
+
+    ([Validating] "Output Knowledge Created": the engine keeps a KV cache with
+    post-verify compaction; [Build] "The Output Knowledge Created": the
+    compaction keeps the accepted tokens for the following steps.)
+
+    Reading: the root (node 0, the last committed token) and the accepted
+    drafts, in path order, become cache positions L_b .. L_b + accept_len of
+    request b; dest_rows[b] is the cache row of position L_b.  The bonus token
+    has no latent row yet (it is the next step's root).  Rows are moved one at
+    a time in path order: position L_b + k receives node accept_nodes[b, k].
+    Because a path's node indices grow with depth, this order is also correct
+    when the tree rows live in the cache itself right after the prefix (row
+    dest_rows[b] + i holding node i): a row is always read before it is
+    overwritten.
+
+    ckv_tree [B, N, Dl] and krope_tree [B, N, Dr] may be views of ckv / krope
+    (that in-place layout); ckv [R, Dl] and krope [R, Dr] are updated.
+    Entries of accept_nodes outside 0..N-1 are skipped; requests with a
+    negative dest row are left alone.
+    """
+    B, N = np.asarray(accept_nodes).shape
+    for b in range(B):
+        d0 = int(dest_rows[b])
+        if d0 < 0:
+            continue
+        for k in range(min(int(accept_len[b]), N - 1) + 1):
+            s = int(accept_nodes[b, k])
+            if not 0 <= s < N:
+                continue
+            ckv[d0 + k, :] = ckv_tree[b, s, :]
+            krope[d0 + k, :] = krope_tree[b, s, :]
+    return ckv, krope

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import build_mask_ref, greedy_accept_ref, target_argmax_ref, verify_attn_ref
+from oracle import build_mask_ref, compact_kv_ref, greedy_accept_ref, target_argmax_ref, verify_attn_ref
 from synth import bounded_tree, chain_tree, make_config, make_workload, uniform_tree
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -484,3 +484,118 @@ def test_longer_branch_beats_earlier_sibling():
     assert alen.tolist() == [2]
     assert nodes[0].tolist() == [0, 2, 3, -1]
     assert commit[0].tolist() == [3, 1, 2, -1]
+
+
+# ----------------------------------------------------------------------------
+# KV-cache compaction after acceptance
+# ----------------------------------------------------------------------------
+
+def accepted_workload(seed, B=3, N=20, L=(7, 0, 12), p_match=0.8, tree=("bounded", 6, 3)):
+    w = make_workload(B=B, N=N, H=2, Dl=8, Dr=4, dtype="f32", std=1.0, scale=0.4, prefix=("list", list(L)),
+                      tree=tree, V=40, p_match=p_match, seed=seed)
+    _, alen, nodes, _ = greedy_accept_ref(w.logits, w.tokens, w.parents)
+    return w, alen, nodes
+
+
+def cache_with_room(w, extra):
+    """Per-request cache regions [L_b + extra rows]; returns (c, r, dest_rows) with the prefix copied in."""
+    kv = w.f32("kv").astype(np.float64)
+    starts, rows = [], 0
+    for b in range(w.B):
+        starts.append(rows)
+        rows += int(w.prefix_lens[b]) + extra
+    c = np.full((rows, w.Dl), np.nan)
+    r = np.full((rows, w.Dr), np.nan)
+    for b in range(w.B):
+        s0, L = int(w.prefix_offsets[b]), int(w.prefix_lens[b])
+        c[starts[b]:starts[b] + L] = kv[s0:s0 + L, :w.Dl]
+        r[starts[b]:starts[b] + L] = kv[s0:s0 + L, w.Dl:]
+    dest = np.array([starts[b] + int(w.prefix_lens[b]) for b in range(w.B)], np.int64)
+    return c, r, dest
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_compaction_rows_sit_at_their_positions(seed):
+    """Cache position L_b + k holds the accepted node whose build_mask position is L_b + k (depth k)."""
+    w, alen, nodes = accepted_workload(seed)
+    _, _, pos, _ = build_mask_ref(w.parents, w.prefix_lens)
+    kt = w.f32("kv_tree").astype(np.float64)
+    c, r, dest = cache_with_room(w, w.N)
+    compact_kv_ref(kt[..., :w.Dl], kt[..., w.Dl:], alen, nodes, c, r, dest)
+    for b in range(w.B):
+        by_pos = {int(pos[b, i]): i for i in range(w.N) if i in set(nodes[b, :alen[b] + 1].tolist())}
+        for k in range(alen[b] + 1):
+            i = by_pos[int(w.prefix_lens[b]) + k]
+            np.testing.assert_array_equal(c[dest[b] + k], kt[b, i, :w.Dl])
+            np.testing.assert_array_equal(r[dest[b] + k], kt[b, i, w.Dl:])
+        assert np.isnan(c[dest[b] + alen[b] + 1:dest[b] + w.N]).all()      # nothing past the path
+        s0 = dest[b] - int(w.prefix_lens[b])
+        kv = w.f32("kv").astype(np.float64)
+        o0 = int(w.prefix_offsets[b])
+        np.testing.assert_array_equal(c[s0:dest[b]], kv[o0:o0 + int(w.prefix_lens[b]), :w.Dl])   # prefix untouched
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_compacted_cache_reproduces_verify_attention(seed):
+    """For every accepted node i at depth k, plain causal attention of i's query over the compacted cache
+    rows up to position L_b + k equals the tree-verify attention of node i (the cache carries the path)."""
+    w, alen, nodes = accepted_workload(seed)
+    _, _, o, lse = run_oracle(w)
+    q, qr, _, _, ct, rt = f64_case(w)
+    c, r, dest = cache_with_room(w, w.N)
+    compact_kv_ref(ct, rt, alen, nodes, c, r, dest)
+    for b in range(w.B):
+        start = dest[b] - int(w.prefix_lens[b])
+        for k in range(alen[b] + 1):
+            i = int(nodes[b, k])
+            end = dest[b] + k + 1
+            K = np.concatenate([c[start:end], r[start:end]], axis=1)
+            Q = np.concatenate([q[b, i], qr[b, i]], axis=1)[:, None, :]
+            ref = sdpa(Q, K, c[start:end], None, w.scale)[:, 0]
+            np.testing.assert_allclose(o[b, i], ref, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(lse[b, i], torch_lse(w.scale * (Q[:, 0] @ K.T), None), rtol=1e-12)
+
+
+def test_compaction_in_place_equals_separate_buffers():
+    """Tree rows stored in the cache right after each prefix (in place) give the same cache as separate
+    tree buffers; the path 0 -> 2 -> 3 -> 4 makes row 2 both a source (depth 1) and a destination (depth 2)."""
+    N, Dl, Dr = 6, 5, 3
+    parents = np.array([[-1, 0, 0, 2, 3, 0]], np.int32)
+    alen = np.array([3], np.int32)
+    nodes = np.array([[0, 2, 3, 4, -1, -1]], np.int32)
+    rng = np.random.default_rng(0)
+    L = 4
+    c = rng.standard_normal((L + N, Dl))
+    r = rng.standard_normal((L + N, Dr))
+    tree_c, tree_r = c[L:].copy()[None], r[L:].copy()[None]
+    c_sep, r_sep = c.copy(), r.copy()
+    compact_kv_ref(tree_c, tree_r, alen, nodes, c_sep, r_sep, np.array([L]))
+    c_in, r_in = c.copy(), r.copy()
+    compact_kv_ref(c_in[L:][None], r_in[L:][None], alen, nodes, c_in, r_in, np.array([L]))   # views of the cache
+    np.testing.assert_array_equal(c_in[:L + 4], c_sep[:L + 4])
+    np.testing.assert_array_equal(r_in[:L + 4], r_sep[:L + 4])
+    np.testing.assert_array_equal(c_sep[L:L + 4], tree_c[0, [0, 2, 3, 4]])
+    assert parents[0, 2] == 0 and parents[0, 3] == 2 and parents[0, 4] == 3
+
+
+def test_compaction_edge_cases():
+    """accept_len 0 moves only the root; a negative dest row leaves the request alone; invalid node
+    entries are skipped; a fully accepted chain stored in place leaves the cache unchanged."""
+    N, Dl, Dr = 4, 3, 2
+    rng = np.random.default_rng(1)
+    tree_c, tree_r = rng.standard_normal((3, N, Dl)), rng.standard_normal((3, N, Dr))
+    c, r = np.zeros((12, Dl)), np.zeros((12, Dr))
+    compact_kv_ref(tree_c, tree_r, np.array([0, 2, 3]), np.array([[0, -1, -1, -1], [0, 9, 1, -1], [0, 1, 2, 3]]),
+                   c, r, np.array([1, 6, -1]))
+    np.testing.assert_array_equal(c[1], tree_c[0, 0])
+    np.testing.assert_array_equal(c[6], tree_c[1, 0])
+    np.testing.assert_array_equal(c[8], tree_c[1, 1])
+    np.testing.assert_array_equal(r[8], tree_r[1, 1])
+    assert not c[[0, 2, 3, 4, 5, 7, 9, 10, 11]].any()
+    c2 = rng.standard_normal((3 + N, Dl))
+    r2 = rng.standard_normal((3 + N, Dr))
+    before_c, before_r = c2.copy(), r2.copy()
+    compact_kv_ref(c2[3:][None], r2[3:][None], np.array([N - 1]), np.arange(N, dtype=np.int32)[None], c2, r2,
+                   np.array([3]))
+    np.testing.assert_array_equal(c2, before_c)
+    np.testing.assert_array_equal(r2, before_r)
