@@ -115,6 +115,31 @@ def cpu_baseline(w, budget_s):
             "seconds": round(elapsed, 2)}
 
 
+def time_compaction(dd, torch, w, kv_tree, accept_len, accept_nodes, steps):
+    """Post-verify KV-cache compaction of this step's accepted paths (outside the timed step): each request's
+    path rows go to its own N-row region of a scratch cache.  Latency-bound: a few KB per request."""
+    dev = kv_tree.device
+    cache = torch.zeros((w.B * w.N, w.Dl + w.Dr), dtype=kv_tree.dtype, device=dev)
+    dest = torch.arange(w.B, dtype=torch.int64, device=dev) * w.N
+    args = (kv_tree[..., :w.Dl], kv_tree[..., w.Dl:], accept_len, accept_nodes, dest, cache[:, :w.Dl],
+            cache[:, w.Dl:])
+    dd.ddtree_compact_kv(*args)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total_ms = 0.0
+    for _ in range(steps):
+        # a GPU-side spin ahead of the events keeps the host's call overhead out of the measured interval
+        torch.cuda._sleep(200000)
+        e0.record(stream)
+        dd.ddtree_compact_kv(*args)
+        e1.record(stream)
+        e1.synchronize()
+        total_ms += e0.elapsed_time(e1)
+    rows = int(accept_len.sum()) + w.B
+    return {"us_per_call": round(total_ms * 1e3 / steps, 2), "rows_moved": rows,
+            "bytes_moved": 2 * rows * (w.Dl + w.Dr) * kv_tree.element_size()}
+
+
 def traffic_for_current_kernel(launch_flops):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this kernel."""
     try:
@@ -244,6 +269,7 @@ def main():
         gbps = accept_bytes / (acc_ms * 1e-3) / 1e9
         out["accept_hbm_gbps"] = round(gbps, 1)
         out["accept_hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
+        out["compact_kv"] = time_compaction(dd, torch, w, kv_tree, acc_out[1], acc_out[2], args.steps)
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     out["input_generation_s"] = round(gen_s, 1)

@@ -167,6 +167,45 @@ int ddtree_greedy_accept(const float* logits, int64_t ld_logits, const int32_t* 
                          int32_t B, int32_t N, int32_t V, int32_t* target_argmax, int32_t* accept_len,
                          int32_t* accept_nodes, int32_t* commit_tokens, void* stream);
 
+/*
+ * ddtree_compact_kv -- move the accepted path's latent rows into the cache.
+ *
+ * After verification the engine compacts its KV cache so that the accepted
+ * tokens carry into the following steps ([Validating] "Output Knowledge
+ * Created": KV cache with post-verify compaction; [Build] "The Output
+ * Knowledge Created").  The root (the last committed token) and the accepted
+ * drafts become cache positions L_b .. L_b + accept_len[b]: for k = 0 ..
+ * accept_len[b], cache row dest_rows[b] + k receives tree row
+ * accept_nodes[b, k] (both the latent and the rotary part).  The bonus token
+ * has no latent row yet; it is the next step's root.
+ *
+ * Rows are moved one at a time in path order.  Because node indices grow
+ * along a path, the call is also correct in place, when node (b, i)'s tree
+ * row is cache row dest_rows[b] + i: for example one call per request with
+ * ckv_tree (krope_tree) pointing at the cache row of position L_b and
+ * ld_ckv_tree = ld_ckv (ld_krope_tree = ld_krope).
+ *
+ *   dtype            DDTREE_F32 or DDTREE_BF16 (rows are copied bit for bit)
+ *   B, N, Dl, Dr     requests, nodes per request (1 .. DDTREE_MAX_NODES), latent
+ *                    and rotary widths (Dl >= 1, Dr >= 0)
+ *   ckv_tree, krope_tree, ld_*_tree  device tree rows, node (b,i) at
+ *                    ckv_tree + (b*N + i)*ld_ckv_tree (as in ddtree_verify_attn)
+ *   accept_len       device int32 [B] from ddtree_greedy_accept (clamped to N-1)
+ *   accept_nodes     device int32 [B, N] from ddtree_greedy_accept; entries
+ *                    outside 0..N-1 are skipped
+ *   dest_rows        device int64 [B]: cache row of position L_b of request b
+ *                    (negative: request skipped)
+ *   ckv, ld_ckv, krope, ld_krope  device cache rows, updated in place; the
+ *                    caller provides room for accept_len + 1 rows per request
+ * Pointers must be aligned to the element size.  The tree rows must not
+ * overlap accept_len, accept_nodes or dest_rows (checked); the cache rows
+ * written must not overlap them either (not checkable on the host).
+ */
+int ddtree_compact_kv(int32_t dtype, int32_t B, int32_t N, int32_t Dl, int32_t Dr, const void* ckv_tree,
+                      int64_t ld_ckv_tree, const void* krope_tree, int64_t ld_krope_tree, const int32_t* accept_len,
+                      const int32_t* accept_nodes, const int64_t* dest_rows, void* ckv, int64_t ld_ckv, void* krope,
+                      int64_t ld_krope, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,8 @@ _SIGNATURES = {
     "ddtree_verify_attn": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _I64, _P, _I64,
                                           _P, _I64, _P, _I64, _P, _F32, _I32, _P, _P, _P, _SZ, _P]),
     "ddtree_greedy_accept": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
+    "ddtree_compact_kv": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P,
+                                         _I64, _P]),
 }
 
 
@@ -212,3 +214,29 @@ def ddtree_greedy_accept(logits: torch.Tensor, tokens: torch.Tensor, parents: to
                                     _ptr(accept_len), _ptr(accept_nodes), _ptr(commit_tokens), _stream(dev, stream))
     _check(st, "ddtree_greedy_accept")
     return target_argmax, accept_len, accept_nodes, commit_tokens
+
+
+def ddtree_compact_kv(ckv_tree: torch.Tensor, krope_tree: torch.Tensor, accept_len: torch.Tensor,
+                      accept_nodes: torch.Tensor, dest_rows: torch.Tensor, ckv: torch.Tensor, krope: torch.Tensor, *,
+                      stream=None) -> None:
+    """Move each request's accepted path rows (root first) to cache rows dest_rows[b] + k, in place.
+
+    ckv_tree [B,N,Dl] / krope_tree [B,N,Dr] views; accept_len int32 [B] and accept_nodes int32 [B,N] from
+    ddtree_greedy_accept; dest_rows int64 [B]; ckv [R,Dl] / krope [R,Dr] row views of the cache (updated).
+    """
+    B, N, Dl = ckv_tree.shape
+    Dr = krope_tree.shape[-1]
+    code = _dtype_code(ckv_tree)
+    for t in (krope_tree, ckv, krope):
+        assert t.dtype == ckv_tree.dtype, "tree rows and cache must share one dtype"
+    assert accept_len.dtype == torch.int32 and accept_len.is_contiguous() and tuple(accept_len.shape) == (B,)
+    assert accept_nodes.dtype == torch.int32 and accept_nodes.is_contiguous() and tuple(accept_nodes.shape) == (B, N)
+    assert dest_rows.dtype == torch.int64 and dest_rows.is_contiguous() and tuple(dest_rows.shape) == (B,)
+    ld_ct = _tree_ld(ckv_tree, B, N, Dl, "ckv_tree")
+    ld_rt = _tree_ld(krope_tree, B, N, Dr, "krope_tree")
+    ld_c = _rows_ld(ckv, Dl, "ckv")
+    ld_r = _rows_ld(krope, Dr, "krope")
+    st = lib().ddtree_compact_kv(code, B, N, Dl, Dr, _ptr(ckv_tree), ld_ct, _ptr(krope_tree), ld_rt, _ptr(accept_len),
+                                 _ptr(accept_nodes), _ptr(dest_rows), _ptr(ckv), ld_c, _ptr(krope), ld_r,
+                                 _stream(ckv.device, stream))
+    _check(st, "ddtree_compact_kv")

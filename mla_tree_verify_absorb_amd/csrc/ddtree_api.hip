@@ -37,6 +37,17 @@ bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool aligned_to(const void* p, unsigned n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1u)) == 0; }
+
+// Largest copy piece (16, 4 or 2 bytes) that divides the row and both rows' addresses.
+int copy_unit(const void* a, int64_t lda_bytes, const void* b, int64_t ldb_bytes, int64_t row_bytes) {
+  const unsigned units[] = {16u, 4u};
+  for (unsigned u : units)
+    if (row_bytes % u == 0 && lda_bytes % u == 0 && ldb_bytes % u == 0 && aligned_to(a, u) && aligned_to(b, u))
+      return (int)u;
+  return 2;
+}
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool bf16_shape_supported(int Dl, int Dr) { return Dl == kMfmaDl && Dr == kMfmaDr; }
@@ -221,6 +232,53 @@ int ddtree_greedy_accept(const float* logits, int64_t ld_logits, const int32_t* 
   if (any_overlap(outs, 4, ins, 3)) return DDTREE_ERR_INVALID_ARG;
   hipError_t e = launch_accept(logits, ld_logits, tokens, parents, B, N, V, target_argmax, accept_len, accept_nodes,
                                commit_tokens, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
+}
+
+int ddtree_compact_kv(int32_t dtype, int32_t B, int32_t N, int32_t Dl, int32_t Dr, const void* ckv_tree,
+                      int64_t ld_ckv_tree, const void* krope_tree, int64_t ld_krope_tree, const int32_t* accept_len,
+                      const int32_t* accept_nodes, const int64_t* dest_rows, void* ckv, int64_t ld_ckv, void* krope,
+                      int64_t ld_krope, void* stream) {
+  if (dtype != DDTREE_F32 && dtype != DDTREE_BF16) return DDTREE_ERR_UNSUPPORTED;
+  if (B < 0 || N < 1 || Dl < 1 || Dr < 0) return DDTREE_ERR_INVALID_ARG;
+  if (N > DDTREE_MAX_NODES) return DDTREE_ERR_UNSUPPORTED;
+  if (B == 0) return DDTREE_OK;
+  if (!ckv_tree || !ckv || !accept_len || !accept_nodes || !dest_rows) return DDTREE_ERR_INVALID_ARG;
+  if (Dr > 0 && (!krope_tree || !krope)) return DDTREE_ERR_INVALID_ARG;
+  if (ld_ckv_tree < Dl || ld_ckv < Dl || (Dr > 0 && (ld_krope_tree < Dr || ld_krope < Dr)))
+    return DDTREE_ERR_INVALID_ARG;
+  const int64_t es = dtype == DDTREE_BF16 ? 2 : 4;
+  if (!aligned_to(ckv_tree, (unsigned)es) || !aligned_to(ckv, (unsigned)es) ||
+      (Dr > 0 && (!aligned_to(krope_tree, (unsigned)es) || !aligned_to(krope, (unsigned)es))))
+    return DDTREE_ERR_INVALID_ARG;
+  const uint64_t n = (uint64_t)B * N;
+  const Range ctrl[] = {range_of(accept_len, (uint64_t)B * 4), range_of(accept_nodes, n * 4),
+                        range_of(dest_rows, (uint64_t)B * 8)};
+  const Range trees[] = {range_of(ckv_tree, ((n - 1) * ld_ckv_tree + Dl) * es),
+                         range_of(krope_tree, Dr ? ((n - 1) * ld_krope_tree + Dr) * es : 0)};
+  // the tree rows (which may interleave, as views of one fused row) must not alias the path arrays
+  for (const Range& t : trees)
+    for (const Range& c : ctrl)
+      if (overlaps(t, c)) return DDTREE_ERR_INVALID_ARG;
+  CompactArgs a{};
+  a.B = B;
+  a.N = N;
+  a.ckv_tree = static_cast<const unsigned char*>(ckv_tree);
+  a.ld_ckv_tree = ld_ckv_tree * es;
+  a.krope_tree = static_cast<const unsigned char*>(krope_tree);
+  a.ld_krope_tree = ld_krope_tree * es;
+  a.accept_len = accept_len;
+  a.accept_nodes = accept_nodes;
+  a.ckv = static_cast<unsigned char*>(ckv);
+  a.ld_ckv = ld_ckv * es;
+  a.krope = static_cast<unsigned char*>(krope);
+  a.ld_krope = ld_krope * es;
+  a.dest_rows = dest_rows;
+  a.c_bytes = Dl * es;
+  a.r_bytes = Dr * es;
+  a.c_unit = copy_unit(ckv_tree, a.ld_ckv_tree, ckv, a.ld_ckv, a.c_bytes);
+  a.r_unit = Dr > 0 ? copy_unit(krope_tree, a.ld_krope_tree, krope, a.ld_krope, a.r_bytes) : 2;
+  hipError_t e = launch_compact_kv(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
 }
 

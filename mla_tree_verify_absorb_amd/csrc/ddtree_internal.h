@@ -45,8 +45,27 @@ constexpr int kRowsPerBlock = 128;   // query rows (node, head) per workgroup
 constexpr int kKeysPerTile = 32;     // latent KV rows per LDS tile
 constexpr int64_t kMaxBf16RowStride = int64_t(1) << 24;   // elements; keeps tile row offsets in 32 bits
 
+// KV-cache compaction (byte addressing; strides in bytes)
+struct CompactArgs {
+  int B, N;
+  const unsigned char* ckv_tree;
+  int64_t ld_ckv_tree;
+  const unsigned char* krope_tree;
+  int64_t ld_krope_tree;
+  const int32_t* accept_len;
+  const int32_t* accept_nodes;
+  unsigned char* ckv;
+  int64_t ld_ckv;
+  unsigned char* krope;
+  int64_t ld_krope;
+  const int64_t* dest_rows;
+  int64_t c_bytes, r_bytes;   // bytes per latent / rotary row
+  int c_unit, r_unit;         // copy piece: 16, 4 or 2 bytes
+};
+
 hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_verify_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_compact_kv(const CompactArgs& a, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace ddtree

@@ -160,3 +160,32 @@ def test_binding_refuses_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "_LIB_PATH", "/nonexistent/libddtree.so")
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+# ---------------------------------------------------------------- compact_kv
+
+def compact(dtype=BF16, B=2, N=16, Dl=512, Dr=64, ct=A + (1 << 24), ld_ct=576, rt=A + (1 << 24) + 1024, ld_rt=576,
+            alen=A, nodes=A + 4096, dest=A + 8192, c=A + (2 << 24), ld_c=576, r=A + (2 << 24) + 1024, ld_r=576):
+    return dd.lib().ddtree_compact_kv(dtype, B, N, Dl, Dr, ct, ld_ct, rt, ld_rt, alen, nodes, dest, c, ld_c, r, ld_r,
+                                      None)
+
+
+def test_compact_kv_validation():
+    assert compact(dtype=5) == UNSUPPORTED
+    assert compact(N=257) == UNSUPPORTED
+    assert compact(N=0) == INVALID
+    assert compact(B=-1) == INVALID
+    assert compact(Dl=0) == INVALID
+    assert compact(Dr=-1) == INVALID
+    assert compact(B=0) == OK                          # nothing enqueued
+    assert compact(ct=None) == INVALID
+    assert compact(c=None) == INVALID
+    assert compact(alen=None) == INVALID
+    assert compact(nodes=None) == INVALID
+    assert compact(dest=None) == INVALID
+    assert compact(rt=None) == INVALID                 # a rotary part needs its rows
+    assert compact(ld_ct=500) == INVALID               # stride shorter than a row
+    assert compact(ld_r=60) == INVALID
+    assert compact(ct=A + (1 << 24) + 1) == INVALID     # not aligned to the bf16 element
+    assert compact(dtype=F32, c=A + (2 << 24) + 2) == INVALID
+    assert compact(nodes=A + (1 << 24) + 64) == INVALID   # tree rows overlap the path arrays

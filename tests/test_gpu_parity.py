@@ -234,3 +234,185 @@ def test_attn_bf16_large_score_jump(jump_key):
         o, lse = dw.attn(mask, num_splits=s)
         torch.cuda.synchronize()
         compare_attn(w, o, lse, *oracle_attn(w, m_ref))
+
+
+# ---------------------------------------------------------------- KV-cache compaction
+
+SENTINEL = {"f32": np.float32(-12345.5), "bf16": np.uint16(0x7FC1)}
+
+
+def host_rows(w, arr):
+    """Raw host rows of a workload array (uint16 bf16 bits or float32), as stored on the device."""
+    return np.ascontiguousarray(arr)
+
+
+def cache_regions(w, extra):
+    """Per-request cache regions of L_b + extra rows, prefix copied in, the rest a sentinel.
+    Returns (host cache [R, Dl+Dr] in raw storage type, dest_rows int64 [B])."""
+    kv = host_rows(w, w.kv)
+    starts, R = [], 0
+    for b in range(w.B):
+        starts.append(R)
+        R += int(w.prefix_lens[b]) + extra
+    cache = np.full((R, w.Dl + w.Dr), SENTINEL[w.dtype], dtype=kv.dtype)
+    for b in range(w.B):
+        s0, L = int(w.prefix_offsets[b]), int(w.prefix_lens[b])
+        cache[starts[b]:starts[b] + L] = kv[s0:s0 + L]
+    dest = np.array([starts[b] + int(w.prefix_lens[b]) for b in range(w.B)], np.int64)
+    return cache, dest
+
+
+def to_dev_raw(arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(arr).to("cuda:0")
+
+
+def from_dev_raw(t, dtype):
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def run_compaction(w, dw, alen, nodes, extra=None, check_rows=None):
+    """GPU compaction of (alen, nodes) into fresh per-request regions vs the oracle; bit-exact."""
+    from oracle import compact_kv_ref
+    extra = w.N if extra is None else extra
+    cache, dest = cache_regions(w, extra)
+    dev_cache = to_dev_raw(cache, w.dtype)
+    dd.ddtree_compact_kv(dw.ckv_tree, dw.krope_tree, torch.from_numpy(np.ascontiguousarray(alen, np.int32)).cuda(),
+                         torch.from_numpy(np.ascontiguousarray(nodes, np.int32)).cuda(), torch.from_numpy(dest).cuda(),
+                         dev_cache[:, :w.Dl], dev_cache[:, w.Dl:])
+    torch.cuda.synchronize()
+    kt = host_rows(w, w.kv_tree)
+    exp = cache.copy()
+    compact_kv_ref(kt[..., :w.Dl], kt[..., w.Dl:], alen, nodes, exp[:, :w.Dl], exp[:, w.Dl:], dest)
+    got = from_dev_raw(dev_cache, w.dtype)
+    rows = slice(None) if check_rows is None else check_rows(dest)
+    assert np.array_equal(got[rows].view(np.uint8), exp[rows].view(np.uint8))
+    return got, exp, dest
+
+
+def random_paths(w, seed):
+    """A random terminal per request and its root path, in the accept outputs' format."""
+    rng = np.random.default_rng(seed)
+    alen = np.zeros(w.B, np.int32)
+    nodes = np.full((w.B, w.N), -1, np.int32)
+    for b in range(w.B):
+        path = [int(rng.integers(0, w.N))]
+        while w.parents[b, path[-1]] != -1:
+            path.append(int(w.parents[b, path[-1]]))
+        path = path[::-1]
+        alen[b] = len(path) - 1
+        nodes[b, :len(path)] = path
+    return alen, nodes
+
+
+@pytest.mark.parametrize("k", [1, 2, 5])
+def test_compact_kv_after_accept(k):
+    """Compaction fed with the GPU accept outputs (equal to the oracle's) moves the accepted rows."""
+    w, dw = config(k)
+    _, alen_t, nodes_t, _ = dd.ddtree_greedy_accept(dw.logits, dw.tokens, dw.parents)
+    _, alen, nodes, _ = check_accept(dw)
+    assert np.array_equal(alen_t.cpu().numpy(), alen) and np.array_equal(nodes_t.cpu().numpy(), nodes)
+    if k == 5:      # compare the regions around the written rows (the cache is 0.6 GB)
+        sel = lambda dest: np.concatenate([np.arange(d - 64, d + w.N) for d in dest])
+        run_compaction(w, dw, alen, nodes, check_rows=sel)
+    else:
+        run_compaction(w, dw, alen, nodes)
+
+
+@pytest.mark.parametrize("k,seed", [(2, 7), (3, 1), (3, 2), (4, 3)])
+def test_compact_kv_random_paths(k, seed):
+    w, dw = config(k)
+    alen, nodes = random_paths(w, seed)
+    if k == 4:
+        sel = lambda dest: np.concatenate([np.arange(d - 16, d + w.N) for d in dest])
+        run_compaction(w, dw, alen, nodes, check_rows=sel)
+    else:
+        run_compaction(w, dw, alen, nodes)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Dl,Dr", [(512, 64), (64, 32), (7, 0), (9, 3)])
+def test_compact_kv_widths_and_edges(dtype, Dl, Dr):
+    """Widths that force 16-, 4- and 2-byte copy pieces; accept_len 0, an invalid node entry (skipped),
+    a negative dest row (request skipped) and a full-depth chain."""
+    N = 12
+    parents = np.array([[-1] + list(range(N - 1)), [-1, 0, 0, 1, 3, 2, 5, 6, 6, 8, 1, 4],
+                        [-1, 0, 1, 1, 2, 4, 4, 6, 7, 0, 9, 10], [-1] + list(range(N - 1))], np.int32)
+    w = make_workload(B=4, N=N, H=1, Dl=Dl, Dr=Dr, dtype=dtype, std=1.0, scale=1.0,
+                      prefix=("list", [5, 0, 33, 2]), tree=("given", parents), seed=11)
+    dw = DevWorkload(w)
+    alen = np.array([0, 3, 5, N - 1], np.int32)
+    nodes = np.full((4, N), -1, np.int32)
+    nodes[0, 0] = 0
+    nodes[1, :4] = [0, 1, 3, 4]
+    nodes[2, :6] = [0, 1, 99, 4, 5, 6]          # entry 99 is skipped
+    nodes[3, :] = np.arange(N)
+    got, exp, dest = run_compaction(w, dw, alen, nodes)
+    # the untouched request: negative dest row
+    cache, dest = cache_regions(w, N)
+    dev_cache = to_dev_raw(cache, dtype)
+    dest_neg = dest.copy()
+    dest_neg[1] = -1
+    dd.ddtree_compact_kv(dw.ckv_tree, dw.krope_tree, torch.from_numpy(alen).cuda(), torch.from_numpy(nodes).cuda(),
+                         torch.from_numpy(dest_neg).cuda(), dev_cache[:, :Dl], dev_cache[:, Dl:])
+    torch.cuda.synchronize()
+    got2 = from_dev_raw(dev_cache, dtype)
+    b1 = slice(int(dest[1]), int(dest[1]) + N)
+    assert np.array_equal(got2[b1].view(np.uint8), cache[b1].view(np.uint8))
+    assert np.array_equal(got2[:int(dest[1])].view(np.uint8), got[:int(dest[1])].view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seed,N,tree", [(0, 40, ("bounded", 8, 3)), (1, 40, ("bounded", 8, 3)),
+                                         (2, 40, ("bounded", 8, 3)), (3, 100, ("chain",))])
+def test_compact_kv_in_place(dtype, seed, N, tree):
+    """Tree rows stored in the cache right after the prefix (node i at row dest + i), one call per request:
+    the in-place move equals the oracle's move between separate buffers.  The 100-node chain is too long
+    to stage in LDS and takes the row-by-row path."""
+    from oracle import compact_kv_ref
+    Dl, Dr = 512, 64
+    w = make_workload(B=3, N=N, H=1, Dl=Dl, Dr=Dr, dtype=dtype, std=1.0, scale=1.0, prefix=("list", [17, 0, 64]),
+                      tree=tree, seed=seed)
+    alen, nodes = random_paths(w, seed + 100)
+    if tree[0] == "chain":
+        alen[:] = N - 1
+        nodes[:] = np.arange(N)
+    if seed == 0:          # the path 0 -> 2 -> 3 -> 4 reads row 2 (depth 1) before writing it (depth 2)
+        w.parents[0, :5] = [-1, 0, 0, 2, 3]
+        alen[0], nodes[0] = 3, -1
+        nodes[0, :4] = [0, 2, 3, 4]
+    cache, dest = cache_regions(w, N)
+    kt = host_rows(w, w.kv_tree)
+    for b in range(w.B):
+        cache[dest[b]:dest[b] + N] = kt[b]          # tree rows in place
+    exp = cache.copy()
+    compact_kv_ref(kt[..., :Dl], kt[..., Dl:], alen, nodes, exp[:, :Dl], exp[:, Dl:], dest)
+    dev_cache = to_dev_raw(cache, dtype)
+    for b in range(w.B):
+        d = int(dest[b])
+        tree_c = dev_cache[d:d + N, :Dl].unsqueeze(0)
+        tree_r = dev_cache[d:d + N, Dl:].unsqueeze(0)
+        dd.ddtree_compact_kv(tree_c, tree_r, torch.from_numpy(alen[b:b + 1].copy()).cuda(),
+                             torch.from_numpy(nodes[b:b + 1].copy()).cuda(), torch.tensor([d], dtype=torch.int64).cuda(),
+                             dev_cache[:, :Dl], dev_cache[:, Dl:])
+    torch.cuda.synchronize()
+    got = from_dev_raw(dev_cache, dtype)
+    for b in range(w.B):
+        rows = slice(int(dest[b]), int(dest[b]) + int(alen[b]) + 1)
+        assert np.array_equal(got[rows].view(np.uint8), exp[rows].view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_compact_kv_long_paths_separate_buffers(dtype):
+    """Paths too long for the LDS stage (a 160-node chain) take the row-by-row path."""
+    N = 160
+    w = make_workload(B=2, N=N, H=1, Dl=512, Dr=64, dtype=dtype, std=1.0, scale=1.0, prefix=("list", [3, 40]),
+                      tree=("chain",), seed=5)
+    dw = DevWorkload(w)
+    alen = np.array([N - 1, 77], np.int32)
+    nodes = np.tile(np.arange(N, dtype=np.int32), (2, 1))
+    nodes[1, 78:] = -1
+    run_compaction(w, dw, alen, nodes)
