@@ -245,3 +245,57 @@ def compact_kv_ref(ckv_tree, krope_tree, accept_len, accept_nodes, ckv, krope, d
             ckv[d0 + k, :] = ckv_tree[b, s, :]
             krope[d0 + k, :] = krope_tree[b, s, :]
     return ckv, krope
+
+
+# ----------------------------------------------------------------------------
+# Best-first draft-tree builder
+# ----------------------------------------------------------------------------
+
+def build_tree_ref(root_tokens, cand_tokens, cand_logp, N):
+    """Grow each request's draft tree best-first from per-depth drafter proposals.
+
+    (The pages' engine builds the draft tree on the GPU best-first, replacing a
+    per-request CPU heap: [Validating] opening and "Output Knowledge
+    Created"; [Truth] opening.  They give no further detail; the reading
+    below is the plainest one.)
+
+    Reading: depth d (1..D) offers K proposals (token, log-probability), the
+    log-probabilities non-increasing along K.  Any node at depth d-1 may take
+    any depth-d proposal as a child; a node's score is its parent's score plus
+    the proposal's log-probability (float32, added root to leaf), the root
+    scoring 0.  Nodes are taken in order of the key (score descending, then
+    depth, parent index and proposal rank ascending) until N nodes exist.  A
+    max-heap holds the frontier; after taking node (parent p, depth d, rank
+    j) it receives the next sibling (p, d, j + 1) and the first child
+    (new node, d + 1, 0).  Taken nodes are numbered in order, so every parent
+    precedes its children.
+
+    Returns parents, tokens, depth (int32 [B, N]) and scores (float32 [B, N]).
+    """
+    import heapq
+    root_tokens = np.asarray(root_tokens)
+    cand_tokens = np.asarray(cand_tokens)
+    cand_logp = np.asarray(cand_logp, dtype=np.float32)
+    B, D, K = cand_tokens.shape
+    parents = np.full((B, N), -1, np.int32)
+    tokens = np.full((B, N), -1, np.int32)
+    depth = np.zeros((B, N), np.int32)
+    scores = np.zeros((B, N), np.float32)
+    for b in range(B):
+        tokens[b, 0] = root_tokens[b]
+        node_score = [np.float32(0.0)]
+        heap = [(-(np.float32(0.0) + cand_logp[b, 0, 0]), 1, 0, 0)]
+        n = 1
+        while n < N and heap:
+            neg, d, p, j = heapq.heappop(heap)
+            s = np.float32(-neg)
+            parents[b, n], tokens[b, n], depth[b, n], scores[b, n] = p, cand_tokens[b, d - 1, j], d, s
+            node_score.append(s)
+            if j + 1 < K:
+                heapq.heappush(heap, (-(node_score[p] + cand_logp[b, d - 1, j + 1]), d, p, j + 1))
+            if d < D:
+                heapq.heappush(heap, (-(s + cand_logp[b, d, 0]), d + 1, n, 0))
+            n += 1
+        if n < N:
+            raise ValueError(f"request {b}: only {n} nodes can be built from {D} depths of {K} proposals")
+    return parents, tokens, depth, scores

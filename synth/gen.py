@@ -273,3 +273,53 @@ def restrict(w: Workload, b: int, n: int) -> Workload:
                     logits=None if w.logits is None else w.logits[b:b + 1, :n],
                     tokens=None if w.tokens is None else w.tokens[b:b + 1, :n],
                     winners=None if w.winners is None else w.winners[b:b + 1, :n], V=w.V)
+
+
+# ----------------------------------------------------------------------------
+# drafter candidates for the best-first tree builder
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class DraftCandidates:
+    """Per-request, per-depth top-K drafter proposals (the tree builder's input).
+
+    root_tokens  int32 [B]        the last committed token (tree node 0)
+    cand_tokens  int32 [B, D, K]  candidate tokens for depth d+1, distinct within a depth
+    cand_logp    float32 [B, D, K] their log-probabilities, <= 0, non-increasing along K
+    golden       int32 [B, D] or None: the tokens placed at rank 0 ("oracle drafter")
+    """
+    root_tokens: np.ndarray
+    cand_tokens: np.ndarray
+    cand_logp: np.ndarray
+    golden: Optional[np.ndarray] = None
+
+
+def make_draft_candidates(*, B: int, D: int, K: int, V: int, seed: int = 0, alpha: float = 0.5,
+                          golden_p: Optional[float] = None, tie_step: Optional[float] = None) -> DraftCandidates:
+    """Seeded drafter proposals.
+
+    Probabilities per depth: a Dirichlet(alpha) draw over K + 1 categories (the last one stands for the
+    rest of the vocabulary), the K proposal probabilities sorted in decreasing order; tokens: K distinct
+    draws from the vocabulary.  golden_p: the rank-0 probability is set to this value and the others
+    rescaled below it, the pages' "oracle drafter" proposing the golden continuation with the highest
+    probability and distractors elsewhere.  tie_step: log-probabilities rounded down to multiples of this
+    step, which makes many equal scores (tie-breaking cases).
+    Draw order: root tokens, then per request and depth: tokens, Dirichlet draw.
+    """
+    rng = np.random.default_rng(seed)
+    root = rng.integers(0, V, size=B).astype(np.int32)
+    toks = np.empty((B, D, K), np.int32)
+    logp = np.empty((B, D, K), np.float32)
+    for b in range(B):
+        for d in range(D):
+            toks[b, d] = rng.choice(V, size=K, replace=False)
+            p = np.sort(rng.dirichlet(np.full(K + 1, alpha))[:K])[::-1]
+            if golden_p is not None:
+                rest = p[1:] / max(p[1:].sum(), 1e-30) * (1.0 - golden_p) * 0.5
+                p = np.concatenate([[golden_p], np.minimum(rest, golden_p)])
+            lp = np.log(np.maximum(p, 1e-30)).astype(np.float32)
+            if tie_step is not None:
+                lp = (np.floor(lp / tie_step) * tie_step).astype(np.float32)
+            logp[b, d] = np.minimum(np.sort(lp)[::-1], 0.0)
+    golden = toks[:, :, 0].copy() if golden_p is not None else None
+    return DraftCandidates(root_tokens=root, cand_tokens=toks, cand_logp=logp, golden=golden)

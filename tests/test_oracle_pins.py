@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import build_mask_ref, compact_kv_ref, greedy_accept_ref, target_argmax_ref, verify_attn_ref
-from synth import bounded_tree, chain_tree, make_config, make_workload, uniform_tree
+from oracle import build_mask_ref, build_tree_ref, compact_kv_ref, greedy_accept_ref, target_argmax_ref, verify_attn_ref
+from synth import bounded_tree, chain_tree, make_config, make_draft_candidates, make_workload, uniform_tree
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -599,3 +599,139 @@ def test_compaction_edge_cases():
                    np.array([3]))
     np.testing.assert_array_equal(c2, before_c)
     np.testing.assert_array_equal(r2, before_r)
+
+
+# ----------------------------------------------------------------------------
+# best-first draft-tree builder
+# ----------------------------------------------------------------------------
+
+def all_candidate_nodes(cand_tokens, cand_logp):
+    """Every node of the candidate tree of one request, by enumeration: (key, path of ranks, tokens, score),
+    with the float32 score summed root to leaf."""
+    D, K = cand_tokens.shape
+    out = []
+
+    def rec(ranks, score, parent_key):
+        d = len(ranks)
+        if d == D:
+            return
+        for j in range(K):
+            sc = np.float32(score + cand_logp[d, j])
+            path = ranks + [j]
+            out.append((sc, path))
+            rec(path, sc, None)
+
+    rec([], np.float32(0.0), None)
+    return out
+
+
+def topk_by_definition(cand_tokens, cand_logp, N):
+    """Root plus the N-1 best candidate nodes under the key (score desc, depth, parent node, rank).  The
+    parent node index is the parent's own position in that order, so rank the nodes level by level."""
+    nodes = all_candidate_nodes(cand_tokens, cand_logp)
+    chosen = {(): 0}                   # rank path -> node index
+    order = []
+    remaining = list(nodes)
+    while len(order) < N - 1:
+        # the best node whose parent is already chosen (the only ones the key can rank next)
+        best = None
+        for sc, path in remaining:
+            par = tuple(path[:-1])
+            if par not in chosen:
+                continue
+            key = (-sc, len(path), chosen[par], path[-1])
+            if best is None or key < best[0]:
+                best = (key, sc, path)
+        key, sc, path = best
+        chosen[tuple(path)] = len(order) + 1
+        order.append((chosen[tuple(path[:-1])], int(cand_tokens[len(path) - 1, path[-1]]), len(path), sc))
+        remaining = [(x, p) for x, p in remaining if p != path]
+    return order
+
+
+@pytest.mark.parametrize("seed,D,K,N", [(0, 3, 3, 12), (1, 4, 2, 20), (2, 2, 5, 25), (3, 5, 3, 40), (4, 3, 4, 2)])
+def test_tree_builder_equals_ranked_enumeration(seed, D, K, N):
+    """The heap build equals ranking every candidate node of the (tiny) candidate tree by the key."""
+    c = make_draft_candidates(B=2, D=D, K=K, V=60, seed=seed)
+    parents, tokens, depth, scores = build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, N)
+    for b in range(2):
+        ref = topk_by_definition(c.cand_tokens[b], c.cand_logp[b], N)
+        got = [(int(parents[b, n]), int(tokens[b, n]), int(depth[b, n]), scores[b, n]) for n in range(1, N)]
+        assert got == ref
+        assert tokens[b, 0] == c.root_tokens[b] and parents[b, 0] == -1 and depth[b, 0] == 0
+
+
+def test_tree_builder_ties_follow_the_key():
+    """Log-probabilities on a coarse grid make many equal scores; the order is still the key's."""
+    c = make_draft_candidates(B=3, D=4, K=3, V=40, seed=9, tie_step=0.5)
+    parents, tokens, depth, scores = build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, 30)
+    assert len(set(np.round(scores[0], 6))) < 30                # ties do occur
+    for b in range(3):
+        ref = topk_by_definition(c.cand_tokens[b], c.cand_logp[b], 30)
+        assert [(int(parents[b, n]), int(tokens[b, n]), int(depth[b, n]), scores[b, n]) for n in range(1, 30)] == ref
+
+
+def test_tree_builder_single_proposal_is_a_chain():
+    c = make_draft_candidates(B=2, D=8, K=1, V=100, seed=3)
+    parents, tokens, depth, scores = build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, 9)
+    for b in range(2):
+        assert parents[b].tolist() == chain_tree(9).tolist()
+        assert tokens[b, 1:].tolist() == c.cand_tokens[b, :, 0].tolist()
+        assert depth[b].tolist() == list(range(9))
+        np.testing.assert_allclose(scores[b, 1:], np.cumsum(c.cand_logp[b, :, 0], dtype=np.float64), rtol=1e-6)
+
+
+def test_tree_builder_oracle_drafter_block_of_8():
+    """An "oracle drafter" (golden token at rank 0 with probability 0.9, distractors far below) over the
+    block's block_size - 1 draft depths (node 0 is the last committed token) makes the golden continuation
+    nodes 1..7, a chain; the greedy accept of a target that agrees with it takes all of them and commits
+    block_size = 8 tokens per verify step, the pages' figure (golden fixture)."""
+    golden_doc = json.load(open(os.path.join(GOLDEN, "pages_chain8_block.json")))
+    block = int(golden_doc["block_size"])
+    D = block - 1
+    V = int(golden_doc["vocab"])
+    c = make_draft_candidates(B=2, D=D, K=4, V=V, seed=5, golden_p=0.9)
+    N = 24
+    parents, tokens, depth, _ = build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, N)
+    for b in range(2):
+        assert parents[b, 1:D + 1].tolist() == list(range(D))
+        assert tokens[b, 1:D + 1].tolist() == c.golden[b].tolist()
+    # target logits whose argmax at node i is the golden token of depth(i) + 1 (and something else below)
+    logits = np.zeros((2, N, V), np.float32)
+    for b in range(2):
+        for i in range(N):
+            logits[b, i, c.golden[b, depth[b, i]] if depth[b, i] < D else 0] = 5.0
+    _, alen, nodes, commit = greedy_accept_ref(logits, tokens, parents)
+    assert alen.tolist() == [D, D]
+    assert nodes[0, :D + 1].tolist() == list(range(D + 1))
+    assert ((commit >= 0).sum(axis=1) == golden_doc["tokens_per_verify_step"]).all()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tree_builder_structure(seed):
+    c = make_draft_candidates(B=4, D=6, K=4, V=500, seed=seed)
+    parents, tokens, depth, scores = build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, 64)
+    for b in range(4):
+        assert tree_is_valid_np(parents[b])
+        for n in range(1, 64):
+            p = parents[b, n]
+            assert depth[b, n] == depth[b, p] + 1
+            assert tokens[b, n] in set(c.cand_tokens[b, depth[b, n] - 1].tolist())
+            assert scores[b, n] <= scores[b, p]
+        kids = {}
+        for n in range(1, 64):
+            kids.setdefault(int(parents[b, n]), []).append(int(tokens[b, n]))
+        assert all(len(v) == len(set(v)) for v in kids.values())        # siblings carry distinct tokens
+        _, dep, _, ok = build_mask_ref(parents[b:b + 1], None)
+        assert ok[0] == 1 and (dep[0] == depth[b]).all()
+
+
+def tree_is_valid_np(p):
+    return p[0] == -1 and all(0 <= p[i] < i for i in range(1, len(p)))
+
+
+def test_tree_builder_rejects_too_small_candidate_trees():
+    c = make_draft_candidates(B=1, D=2, K=2, V=10, seed=0)
+    build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, 7)        # 1 + 2 + 4 nodes exist
+    with pytest.raises(ValueError):
+        build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, 8)
