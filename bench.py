@@ -140,6 +140,30 @@ def time_compaction(dd, torch, w, kv_tree, accept_len, accept_nodes, steps):
             "bytes_moved": 2 * rows * (w.Dl + w.Dr) * kv_tree.element_size()}
 
 
+def time_tree_builder(dd, torch, w, dev, steps, tree_spec):
+    """The best-first draft-tree builder at this workload's tree shape (outside the timed step): N nodes from
+    D draft depths of K proposals each, (D, K) = the workload's depth and branching bounds (12 and 4 for the
+    long-context workload), from seeded synthetic drafter proposals."""
+    from synth import make_draft_candidates
+    D, K = (int(tree_spec[1]), int(tree_spec[2])) if tree_spec[0] == "bounded" else (8, 4)
+    c = make_draft_candidates(B=w.B, D=D, K=K, V=max(w.V, 1000), seed=1)
+    args = (torch.from_numpy(c.root_tokens).to(dev), torch.from_numpy(c.cand_tokens).to(dev),
+            torch.from_numpy(c.cand_logp).to(dev), w.N)
+    dd.ddtree_build_tree(*args)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total_ms = 0.0
+    for _ in range(steps):
+        torch.cuda._sleep(200000)          # keeps the host's call overhead out of the measured interval
+        e0.record(stream)
+        dd.ddtree_build_tree(*args)
+        e1.record(stream)
+        e1.synchronize()
+        total_ms += e0.elapsed_time(e1)
+    return {"us_per_call": round(total_ms * 1e3 / steps, 2), "requests": w.B, "nodes": w.N, "depths": D,
+            "proposals": K}
+
+
 def traffic_for_current_kernel(launch_flops):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this kernel."""
     try:
@@ -270,6 +294,7 @@ def main():
         out["accept_hbm_gbps"] = round(gbps, 1)
         out["accept_hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
         out["compact_kv"] = time_compaction(dd, torch, w, kv_tree, acc_out[1], acc_out[2], args.steps)
+    out["build_tree"] = time_tree_builder(dd, torch, w, dev, args.steps, CONFIGS[args.config]["tree"])
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     out["input_generation_s"] = round(gen_s, 1)

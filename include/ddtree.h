@@ -40,6 +40,8 @@ extern "C" {
 #endif
 
 #define DDTREE_MAX_NODES 256
+#define DDTREE_MAX_DEPTH 64      /* draft depths offered to ddtree_build_tree */
+#define DDTREE_MAX_PROPOSALS 64  /* proposals per depth for ddtree_build_tree */
 
 typedef enum {
   DDTREE_OK = 0,
@@ -205,6 +207,38 @@ int ddtree_compact_kv(int32_t dtype, int32_t B, int32_t N, int32_t Dl, int32_t D
                       int64_t ld_ckv_tree, const void* krope_tree, int64_t ld_krope_tree, const int32_t* accept_len,
                       const int32_t* accept_nodes, const int64_t* dest_rows, void* ckv, int64_t ld_ckv, void* krope,
                       int64_t ld_krope, void* stream);
+
+/*
+ * ddtree_build_tree -- grow each request's draft tree best-first on the GPU.
+ *
+ * The engine builds its draft trees on the GPU best-first, in place of a
+ * per-request CPU heap ([Validating] opening and "Output Knowledge Created").
+ * The pages give no further detail; the reading implemented here: depth d
+ * (1..D) offers K proposals (token, log-probability), the log-probabilities
+ * non-increasing along K.  Any node at depth d-1 may take any depth-d
+ * proposal as a child; a node's score is its parent's score plus the
+ * proposal's log-probability (float32 additions, root to leaf; the root scores
+ * 0).  Nodes are taken in order of the key (score descending, then depth,
+ * parent index, proposal rank ascending) until N nodes exist and are numbered
+ * in that order, so parents precede children and the output is a valid tree
+ * for ddtree_build_mask.  With log-probabilities <= 0 the result is the root
+ * plus the N-1 best nodes of the whole candidate tree under that key.
+ *
+ *   B, N             requests (>= 0), nodes per tree (1 .. DDTREE_MAX_NODES)
+ *   D, K             draft depths (1 .. DDTREE_MAX_DEPTH) and proposals per depth
+ *                    (1 .. DDTREE_MAX_PROPOSALS); N must not exceed the candidate
+ *                    tree's size 1 + K + K^2 + ... + K^D (UNSUPPORTED otherwise)
+ *   root_tokens      device int32 [B]: node 0's token (the last committed token)
+ *   cand_tokens      device int32 [B, D, K]: proposal tokens of depth d+1 at [b, d]
+ *   cand_logp        device float32 [B, D, K]: their log-probabilities (NaN: undefined)
+ *   parents, tokens  device int32 [B, N]: the tree (parent[0] = -1)
+ *   depth            device int32 [B, N] or NULL
+ *   scores           device float32 [B, N] or NULL: each node's score
+ * Outputs must not overlap inputs or each other (checked).
+ */
+int ddtree_build_tree(int32_t B, int32_t N, int32_t D, int32_t K, const int32_t* root_tokens,
+                      const int32_t* cand_tokens, const float* cand_logp, int32_t* parents, int32_t* tokens,
+                      int32_t* depth, float* scores, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,8 @@ DDTREE_ERR_HIP = -4
 DDTREE_F32 = 0
 DDTREE_BF16 = 1
 DDTREE_MAX_NODES = 256
+DDTREE_MAX_DEPTH = 64
+DDTREE_MAX_PROPOSALS = 64
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -41,6 +43,7 @@ _SIGNATURES = {
     "ddtree_greedy_accept": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "ddtree_compact_kv": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P,
                                          _I64, _P]),
+    "ddtree_build_tree": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -240,3 +243,29 @@ def ddtree_compact_kv(ckv_tree: torch.Tensor, krope_tree: torch.Tensor, accept_l
                                  _ptr(accept_nodes), _ptr(dest_rows), _ptr(ckv), ld_c, _ptr(krope), ld_r,
                                  _stream(ckv.device, stream))
     _check(st, "ddtree_compact_kv")
+
+
+def ddtree_build_tree(root_tokens: torch.Tensor, cand_tokens: torch.Tensor, cand_logp: torch.Tensor, N: int, *,
+                      parents: Optional[torch.Tensor] = None, tokens: Optional[torch.Tensor] = None,
+                      depth: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None, stream=None):
+    """Best-first draft trees of N nodes from per-depth proposals cand_tokens / cand_logp [B, D, K].
+
+    Returns (parents int32 [B,N], tokens int32 [B,N], depth int32 [B,N], scores float32 [B,N]).
+    """
+    B, D, K = cand_tokens.shape
+    assert cand_tokens.dtype == torch.int32 and cand_tokens.is_contiguous()
+    assert cand_logp.dtype == torch.float32 and cand_logp.is_contiguous() and tuple(cand_logp.shape) == (B, D, K)
+    assert root_tokens.dtype == torch.int32 and root_tokens.is_contiguous() and tuple(root_tokens.shape) == (B,)
+    dev = cand_tokens.device
+    if parents is None:
+        parents = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if depth is None:
+        depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if scores is None:
+        scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+    st = lib().ddtree_build_tree(B, int(N), D, K, _ptr(root_tokens), _ptr(cand_tokens), _ptr(cand_logp),
+                                 _ptr(parents), _ptr(tokens), _ptr(depth), _ptr(scores), _stream(dev, stream))
+    _check(st, "ddtree_build_tree")
+    return parents, tokens, depth, scores

@@ -282,4 +282,29 @@ int ddtree_compact_kv(int32_t dtype, int32_t B, int32_t N, int32_t Dl, int32_t D
   return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
 }
 
+int ddtree_build_tree(int32_t B, int32_t N, int32_t D, int32_t K, const int32_t* root_tokens,
+                      const int32_t* cand_tokens, const float* cand_logp, int32_t* parents, int32_t* tokens,
+                      int32_t* depth, float* scores, void* stream) {
+  if (B < 0 || N < 1 || D < 1 || K < 1) return DDTREE_ERR_INVALID_ARG;
+  if (N > DDTREE_MAX_NODES || D > DDTREE_MAX_DEPTH || K > DDTREE_MAX_PROPOSALS) return DDTREE_ERR_UNSUPPORTED;
+  // the candidate tree must hold N nodes: 1 + K + ... + K^D (saturated)
+  int64_t size = 1, level = 1;
+  for (int d = 1; d <= D && size < N; ++d) {
+    level = level * K > DDTREE_MAX_NODES ? DDTREE_MAX_NODES : level * K;
+    size += level;
+  }
+  if (size < N) return DDTREE_ERR_UNSUPPORTED;
+  if (B == 0) return DDTREE_OK;
+  if (!root_tokens || !cand_tokens || !cand_logp || !parents || !tokens) return DDTREE_ERR_INVALID_ARG;
+  const uint64_t n = (uint64_t)B * N, c = (uint64_t)B * D * K;
+  const Range ins[] = {range_of(root_tokens, (uint64_t)B * 4), range_of(cand_tokens, c * 4),
+                       range_of(cand_logp, c * 4)};
+  const Range outs[] = {range_of(parents, n * 4), range_of(tokens, n * 4), range_of(depth, depth ? n * 4 : 0),
+                        range_of(scores, scores ? n * 4 : 0)};
+  if (any_overlap(outs, 4, ins, 3)) return DDTREE_ERR_INVALID_ARG;
+  hipError_t e = launch_build_tree(B, N, D, K, root_tokens, cand_tokens, cand_logp, parents, tokens, depth, scores,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
+}
+
 }  // extern "C"

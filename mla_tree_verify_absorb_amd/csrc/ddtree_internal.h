@@ -66,6 +66,9 @@ struct CompactArgs {
 hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_verify_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_compact_kv(const CompactArgs& a, hipStream_t stream);
+hipError_t launch_build_tree(int B, int N, int D, int K, const int32_t* root_tokens, const int32_t* cand_tokens,
+                             const float* cand_logp, int32_t* parents, int32_t* tokens, int32_t* depth, float* scores,
+                             hipStream_t stream);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace ddtree

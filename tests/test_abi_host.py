@@ -189,3 +189,31 @@ def test_compact_kv_validation():
     assert compact(ct=A + (1 << 24) + 1) == INVALID     # not aligned to the bf16 element
     assert compact(dtype=F32, c=A + (2 << 24) + 2) == INVALID
     assert compact(nodes=A + (1 << 24) + 64) == INVALID   # tree rows overlap the path arrays
+
+
+# ---------------------------------------------------------------- build_tree
+
+def btree(B=2, N=64, D=8, K=4, root=A, ct=A + 4096, cl=A + 8192, par=A + 16384, tok=A + 20480, dep=A + 24576,
+          sc=A + 28672):
+    return dd.lib().ddtree_build_tree(B, N, D, K, root, ct, cl, par, tok, dep, sc, None)
+
+
+def test_build_tree_validation():
+    assert btree(N=0) == INVALID
+    assert btree(D=0) == INVALID
+    assert btree(K=0) == INVALID
+    assert btree(B=-1) == INVALID
+    assert btree(N=257) == UNSUPPORTED
+    assert btree(D=65) == UNSUPPORTED
+    assert btree(K=65) == UNSUPPORTED
+    assert btree(B=0, N=7, D=2, K=2) == OK             # 1 + 2 + 4 = 7 nodes fit
+    assert btree(B=0, N=8, D=2, K=2) == UNSUPPORTED    # ... 8 do not
+    assert btree(B=0, N=9, D=8, K=1) == OK             # a chain of 8 draft depths
+    assert btree(B=0, N=10, D=8, K=1) == UNSUPPORTED
+    assert btree(B=0) == OK
+    assert btree(root=None) == INVALID
+    assert btree(cl=None) == INVALID
+    assert btree(par=None) == INVALID
+    assert btree(tok=None) == INVALID
+    assert btree(par=A + 8192 + 64) == INVALID          # parents overlap cand_logp
+    assert btree(dep=A + 16384 + 4) == INVALID          # depth overlaps parents

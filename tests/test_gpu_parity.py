@@ -12,7 +12,7 @@ import torch
 
 import mla_tree_verify_absorb_amd as dd
 from gpu_util import DevWorkload, check_accept, check_mask, compare_attn, mask_np, oracle_attn
-from synth import make_config, make_workload
+from synth import make_config, make_draft_candidates, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -416,3 +416,43 @@ def test_compact_kv_long_paths_separate_buffers(dtype):
     nodes = np.tile(np.arange(N, dtype=np.int32), (2, 1))
     nodes[1, 78:] = -1
     run_compaction(w, dw, alen, nodes)
+
+
+# ---------------------------------------------------------------- best-first tree builder
+
+def check_build_tree(c, N):
+    from oracle import build_tree_ref
+    dev = "cuda:0"
+    got = dd.ddtree_build_tree(torch.from_numpy(c.root_tokens).to(dev), torch.from_numpy(c.cand_tokens).to(dev),
+                               torch.from_numpy(c.cand_logp).to(dev), N)
+    torch.cuda.synchronize()
+    ref = build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, N)
+    for g, r in zip(got, ref):
+        g = g.cpu().numpy()
+        assert np.array_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
+                              r.view(np.uint32) if r.dtype == np.float32 else r)
+    return got
+
+
+@pytest.mark.parametrize("B,D,K,N,seed", [(4, 7, 4, 64, 0), (2, 7, 8, 128, 1), (3, 16, 2, 256, 2), (1, 3, 3, 40, 3),
+                                          (5, 8, 1, 9, 4), (2, 64, 64, 256, 5), (16, 12, 4, 128, 6), (1, 1, 1, 2, 7)])
+def test_build_tree_matches_oracle(B, D, K, N, seed):
+    c = make_draft_candidates(B=B, D=D, K=K, V=1000, seed=seed)
+    check_build_tree(c, N)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_build_tree_ties_and_oracle_drafter(seed):
+    check_build_tree(make_draft_candidates(B=3, D=6, K=5, V=200, seed=seed, tie_step=0.5), 100)
+    c = make_draft_candidates(B=2, D=7, K=4, V=512, seed=seed, golden_p=0.9)
+    parents, tokens, _, _ = check_build_tree(c, 24)
+    assert parents[:, 1:8].cpu().numpy().tolist() == [list(range(7))] * 2
+
+
+def test_build_tree_feeds_build_mask():
+    """The GPU-built trees are valid inputs of ddtree_build_mask, with matching depths."""
+    c = make_draft_candidates(B=4, D=12, K=4, V=5000, seed=11)
+    parents, tokens, depth, _ = check_build_tree(c, 128)
+    mask, mdepth, pos, ok = dd.ddtree_build_mask(parents)
+    torch.cuda.synchronize()
+    assert (ok.cpu() == 1).all() and torch.equal(mdepth.cpu(), depth.cpu())
