@@ -299,3 +299,34 @@ def build_tree_ref(root_tokens, cand_tokens, cand_logp, N):
         if n < N:
             raise ValueError(f"request {b}: only {n} nodes can be built from {D} depths of {K} proposals")
     return parents, tokens, depth, scores
+
+
+# ----------------------------------------------------------------------------
+# NeoX rotary embedding at tree positions
+# ----------------------------------------------------------------------------
+
+def rope_inv_freq(Dr, base):
+    """Plain rotary frequencies base^(-2i/Dr), i = 0 .. Dr/2 - 1, in float64."""
+    return base ** (-np.arange(0, Dr, 2, dtype=np.float64) / Dr)
+
+
+def rope_neox_ref(x, positions, inv_freq):
+    """NeoX-style rotation of the last axis of x at the given positions, in float64.
+
+    (The engine applies NeoX rotary embeddings and computes the angle in
+    double precision: [Truth] "What the Output Tells Us"; positions are
+    cache length plus node depth, int64: [Build] "The Thinking Process
+    Visible in Reasoning".)
+
+    NeoX pairs element i with element i + Dr/2.  With angle
+    a_i = position * inv_freq[i]: out[i] = x[i] cos a_i - x[i + Dr/2] sin a_i and
+    out[i + Dr/2] = x[i + Dr/2] cos a_i + x[i] sin a_i.
+
+    x: [..., Dr]; positions: broadcastable to x.shape[:-1] (int64); returns float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * np.asarray(inv_freq, dtype=np.float64)
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)

@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import build_mask_ref, build_tree_ref, compact_kv_ref, greedy_accept_ref, target_argmax_ref, verify_attn_ref
+from oracle import (build_mask_ref, build_tree_ref, compact_kv_ref, greedy_accept_ref, rope_inv_freq, rope_neox_ref,
+                    target_argmax_ref, verify_attn_ref)
 from synth import bounded_tree, chain_tree, make_config, make_draft_candidates, make_workload, uniform_tree
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -735,3 +736,58 @@ def test_tree_builder_rejects_too_small_candidate_trees():
     build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, 7)        # 1 + 2 + 4 nodes exist
     with pytest.raises(ValueError):
         build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, 8)
+
+
+# ----------------------------------------------------------------------------
+# NeoX rotary embedding at tree positions
+# ----------------------------------------------------------------------------
+
+def test_rope_hand_cases():
+    """A 2-vector turns counterclockwise by the angle; NeoX pairs element i with i + Dr/2 (not 2i, 2i+1)."""
+    for p in (0, 1, 7, 123456789012):
+        out = rope_neox_ref(np.array([1.0, 0.0]), np.int64(p), np.array([1.0]))
+        assert out.tolist() == [math.cos(float(p)), math.sin(float(p))]
+    f = np.array([0.5, 0.25])
+    out = rope_neox_ref(np.array([1.0, 0.0, 0.0, 0.0]), np.int64(3), f)
+    assert out.tolist() == [math.cos(1.5), 0.0, math.sin(1.5), 0.0]
+    out = rope_neox_ref(np.array([0.0, 0.0, 0.0, 1.0]), np.int64(3), f)
+    assert out.tolist() == [0.0, -math.sin(0.75), 0.0, math.cos(0.75)]
+    inv = rope_inv_freq(8, 10000.0)
+    assert inv.tolist() == [1.0, 10000.0 ** -0.25, 10000.0 ** -0.5, 10000.0 ** -0.75]
+
+
+def test_rope_identity_norms_composition_and_relative_position():
+    rng = np.random.default_rng(0)
+    Dr = 64
+    inv = rope_inv_freq(Dr, 10000.0)
+    x = rng.standard_normal((5, Dr))
+    pos = np.array([0, 1, 17, 4096, 131072 + 11], np.int64)
+    np.testing.assert_array_equal(rope_neox_ref(x, np.zeros(5, np.int64), inv), x)
+    y = rope_neox_ref(x, pos, inv)
+    h = Dr // 2
+    np.testing.assert_allclose(y[:, :h] ** 2 + y[:, h:] ** 2, x[:, :h] ** 2 + x[:, h:] ** 2, rtol=1e-12)
+    np.testing.assert_allclose(rope_neox_ref(rope_neox_ref(x, pos, inv), 3 * pos, inv), rope_neox_ref(x, 4 * pos, inv),
+                               rtol=1e-9, atol=1e-9)
+    q, k = rng.standard_normal(Dr), rng.standard_normal(Dr)
+    for pq, pk in [(5, 2), (131083, 131072), (100, 100)]:
+        lhs = rope_neox_ref(q, np.int64(pq), inv) @ rope_neox_ref(k, np.int64(pk), inv)
+        rhs = rope_neox_ref(q, np.int64(pq - pk), inv) @ k
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(rhs))
+
+
+def test_rope_at_tree_positions_makes_verify_shift_invariant():
+    """Rotating the prefix keys at 0..L-1 and the tree queries and keys at L + depth, then verifying, gives
+    the same outputs when every position is shifted by a constant: only relative positions matter."""
+    w = small(3, B=2, N=12, L=(5, 9), tree=("bounded", 4, 3))
+    mask, depth, pos, _ = build_mask_ref(w.parents, w.prefix_lens)
+    q, qr, c, r, ct, rt = f64_case(w)
+    inv = rope_inv_freq(w.Dr, 10000.0)
+    outs = []
+    for shift in (0, 1000):
+        rp = np.concatenate([rope_neox_ref(r[w.prefix_offsets[b]:w.prefix_offsets[b + 1]],
+                                           np.arange(w.prefix_lens[b]) + shift, inv) for b in range(w.B)])
+        qrr = rope_neox_ref(qr, (pos + shift)[:, :, None], inv)
+        rtr = rope_neox_ref(rt, pos + shift, inv)
+        outs.append(verify_attn_ref(q, qrr, c, rp, w.prefix_offsets, ct, rtr, mask, w.scale))
+    np.testing.assert_allclose(outs[0][0], outs[1][0], rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(outs[0][1], outs[1][1], rtol=1e-11)
