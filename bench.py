@@ -115,6 +115,23 @@ def cpu_baseline(w, budget_s):
             "seconds": round(elapsed, 2)}
 
 
+def gpu_time_us(torch, dev, fn, steps):
+    """Mean GPU time of fn() in microseconds: a GPU-side spin ahead of each pair of events keeps the host's
+    call overhead out of the measured interval."""
+    fn()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total_ms = 0.0
+    for _ in range(steps):
+        torch.cuda._sleep(200000)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        total_ms += e0.elapsed_time(e1)
+    return round(total_ms * 1e3 / steps, 2)
+
+
 def time_compaction(dd, torch, w, kv_tree, accept_len, accept_nodes, steps):
     """Post-verify KV-cache compaction of this step's accepted paths (outside the timed step): each request's
     path rows go to its own N-row region of a scratch cache.  Latency-bound: a few KB per request."""
@@ -123,21 +140,9 @@ def time_compaction(dd, torch, w, kv_tree, accept_len, accept_nodes, steps):
     dest = torch.arange(w.B, dtype=torch.int64, device=dev) * w.N
     args = (kv_tree[..., :w.Dl], kv_tree[..., w.Dl:], accept_len, accept_nodes, dest, cache[:, :w.Dl],
             cache[:, w.Dl:])
-    dd.ddtree_compact_kv(*args)
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    total_ms = 0.0
-    for _ in range(steps):
-        # a GPU-side spin ahead of the events keeps the host's call overhead out of the measured interval
-        torch.cuda._sleep(200000)
-        e0.record(stream)
-        dd.ddtree_compact_kv(*args)
-        e1.record(stream)
-        e1.synchronize()
-        total_ms += e0.elapsed_time(e1)
+    us = gpu_time_us(torch, dev, lambda: dd.ddtree_compact_kv(*args), steps)
     rows = int(accept_len.sum()) + w.B
-    return {"us_per_call": round(total_ms * 1e3 / steps, 2), "rows_moved": rows,
-            "bytes_moved": 2 * rows * (w.Dl + w.Dr) * kv_tree.element_size()}
+    return {"us_per_call": us, "rows_moved": rows, "bytes_moved": 2 * rows * (w.Dl + w.Dr) * kv_tree.element_size()}
 
 
 def time_tree_builder(dd, torch, w, dev, steps, tree_spec):
@@ -149,19 +154,20 @@ def time_tree_builder(dd, torch, w, dev, steps, tree_spec):
     c = make_draft_candidates(B=w.B, D=D, K=K, V=max(w.V, 1000), seed=1)
     args = (torch.from_numpy(c.root_tokens).to(dev), torch.from_numpy(c.cand_tokens).to(dev),
             torch.from_numpy(c.cand_logp).to(dev), w.N)
-    dd.ddtree_build_tree(*args)
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    total_ms = 0.0
-    for _ in range(steps):
-        torch.cuda._sleep(200000)          # keeps the host's call overhead out of the measured interval
-        e0.record(stream)
-        dd.ddtree_build_tree(*args)
-        e1.record(stream)
-        e1.synchronize()
-        total_ms += e0.elapsed_time(e1)
-    return {"us_per_call": round(total_ms * 1e3 / steps, 2), "requests": w.B, "nodes": w.N, "depths": D,
-            "proposals": K}
+    us = gpu_time_us(torch, dev, lambda: dd.ddtree_build_tree(*args), steps)
+    return {"us_per_call": us, "requests": w.B, "nodes": w.N, "depths": D, "proposals": K}
+
+
+def time_rope(dd, torch, w, dev, q_rope, kv_tree, positions, steps):
+    """NeoX rotation of the tree nodes' rotary queries (all heads) and keys at their positions (outside the
+    timed step; on copies, so the step's inputs stay as they are)."""
+    import numpy as np
+    q = q_rope.clone()
+    kt = kv_tree.clone()
+    inv = torch.from_numpy(10000.0 ** (-np.arange(0, w.Dr, 2, dtype=np.float64) / w.Dr)).to(dev)
+    us = gpu_time_us(torch, dev, lambda: dd.ddtree_rope_tree(q, kt[..., w.Dl:], positions, inv), steps)
+    rows = w.B * w.N * (w.H + 1)
+    return {"us_per_call": us, "rows": rows, "bytes_moved": 2 * rows * w.Dr * q_rope.element_size()}
 
 
 def traffic_for_current_kernel(launch_flops):
@@ -295,6 +301,7 @@ def main():
         out["accept_hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
         out["compact_kv"] = time_compaction(dd, torch, w, kv_tree, acc_out[1], acc_out[2], args.steps)
     out["build_tree"] = time_tree_builder(dd, torch, w, dev, args.steps, CONFIGS[args.config]["tree"])
+    out["rope_tree"] = time_rope(dd, torch, w, dev, q_rope, kv_tree, positions, args.steps)
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     out["input_generation_s"] = round(gen_s, 1)

@@ -240,6 +240,34 @@ int ddtree_build_tree(int32_t B, int32_t N, int32_t D, int32_t K, const int32_t*
                       const int32_t* cand_tokens, const float* cand_logp, int32_t* parents, int32_t* tokens,
                       int32_t* depth, float* scores, void* stream);
 
+/*
+ * ddtree_rope_tree -- NeoX rotary embedding of the tree nodes at their positions.
+ *
+ * Rotates, in place, each tree node's rotary queries (all heads) and its
+ * rotary key row at the node's position, cache length + depth as produced by
+ * ddtree_build_mask ([Truth] "What the Output Tells Us": NeoX rotary
+ * embeddings with the angle computed in double; [Build] "The Thinking Process
+ * Visible in Reasoning": int64 positions).  Element i pairs with element
+ * i + Dr/2; angle a_i = position * inv_freq[i] in float64;
+ *   out[i] = x[i] cos a_i - x[i+Dr/2] sin a_i,
+ *   out[i+Dr/2] = x[i+Dr/2] cos a_i + x[i] sin a_i,
+ * computed in float64 and rounded once to the storage type.  Run it before
+ * ddtree_verify_attn, whose rotary inputs are taken as already rotated.
+ *
+ *   dtype            DDTREE_F32 or DDTREE_BF16 (storage type of both arrays)
+ *   B, N, H, Dr      requests, nodes (1 .. DDTREE_MAX_NODES), heads, rotary width
+ *                    (even, 2 .. 512)
+ *   q_rope           device [B, N, H, Dr] dense, rotated in place, or NULL
+ *   krope_tree, ld_krope_tree  device rows (b, i) at krope_tree + (b*N + i)*ld,
+ *                    rotated in place, or NULL
+ *   positions        device int64 [B, N]
+ *   inv_freq         device float64 [Dr/2]: the rotary frequencies (any scaling
+ *                    of them is the caller's)
+ * The rotated arrays must not overlap positions or inv_freq (checked).
+ */
+int ddtree_rope_tree(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dr, void* q_rope, void* krope_tree,
+                     int64_t ld_krope_tree, const int64_t* positions, const double* inv_freq, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "ddtree_compact_kv": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P,
                                          _I64, _P]),
     "ddtree_build_tree": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ddtree_rope_tree": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _P]),
 }
 
 
@@ -269,3 +270,26 @@ def ddtree_build_tree(root_tokens: torch.Tensor, cand_tokens: torch.Tensor, cand
                                  _ptr(parents), _ptr(tokens), _ptr(depth), _ptr(scores), _stream(dev, stream))
     _check(st, "ddtree_build_tree")
     return parents, tokens, depth, scores
+
+
+def ddtree_rope_tree(q_rope: Optional[torch.Tensor], krope_tree: Optional[torch.Tensor], positions: torch.Tensor,
+                     inv_freq: torch.Tensor, *, stream=None) -> None:
+    """NeoX rotation, in place, of q_rope [B,N,H,Dr] (dense) and krope_tree [B,N,Dr] rows at positions [B,N]
+    (int64) with float64 frequencies inv_freq [Dr/2].  Either array may be None."""
+    assert positions.dtype == torch.int64 and positions.is_contiguous() and positions.dim() == 2
+    assert inv_freq.dtype == torch.float64 and inv_freq.is_contiguous()
+    B, N = positions.shape
+    ref = q_rope if q_rope is not None else krope_tree
+    Dr = ref.shape[-1]
+    H = 1
+    if q_rope is not None:
+        assert q_rope.is_contiguous() and q_rope.dim() == 4 and tuple(q_rope.shape[:2]) == (B, N)
+        H = q_rope.shape[2]
+    ld = Dr
+    if krope_tree is not None:
+        assert krope_tree.dtype == ref.dtype
+        ld = _tree_ld(krope_tree, B, N, Dr, "krope_tree")
+    assert inv_freq.numel() == Dr // 2
+    st = lib().ddtree_rope_tree(_dtype_code(ref), B, N, H, Dr, _ptr(q_rope), _ptr(krope_tree), ld, _ptr(positions),
+                                _ptr(inv_freq), _stream(ref.device, stream))
+    _check(st, "ddtree_rope_tree")

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libddtree.so")
 SOURCES = ["ddtree_api.hip", "build_mask.hip", "accept.hip", "verify_attn_f32.hip", "verify_attn_bf16.hip",
-           "compact_kv.hip", "build_tree.hip"]
+           "compact_kv.hip", "build_tree.hip", "rope_tree.hip"]
 # Per-file device flags (none at present).
 FILE_FLAGS = {}
 ARCH = "gfx950"

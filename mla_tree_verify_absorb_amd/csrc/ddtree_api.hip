@@ -307,4 +307,35 @@ int ddtree_build_tree(int32_t B, int32_t N, int32_t D, int32_t K, const int32_t*
   return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
 }
 
+int ddtree_rope_tree(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dr, void* q_rope, void* krope_tree,
+                     int64_t ld_krope_tree, const int64_t* positions, const double* inv_freq, void* stream) {
+  if (dtype != DDTREE_F32 && dtype != DDTREE_BF16) return DDTREE_ERR_UNSUPPORTED;
+  if (B < 0 || N < 1 || H < 1 || Dr < 2 || (Dr & 1)) return DDTREE_ERR_INVALID_ARG;
+  if (N > DDTREE_MAX_NODES || Dr > kMaxRopeDim) return DDTREE_ERR_UNSUPPORTED;
+  if (B == 0 || (!q_rope && !krope_tree)) return DDTREE_OK;
+  if (!positions || !inv_freq) return DDTREE_ERR_INVALID_ARG;
+  if (krope_tree && ld_krope_tree < Dr) return DDTREE_ERR_INVALID_ARG;
+  const int64_t es = dtype == DDTREE_BF16 ? 2 : 4;
+  if ((q_rope && !aligned_to(q_rope, (unsigned)es)) || (krope_tree && !aligned_to(krope_tree, (unsigned)es)))
+    return DDTREE_ERR_INVALID_ARG;
+  const uint64_t n = (uint64_t)B * N;
+  const Range ins[] = {range_of(positions, n * 8), range_of(inv_freq, (uint64_t)(Dr / 2) * 8)};
+  const Range outs[] = {range_of(q_rope, q_rope ? n * H * Dr * es : 0),
+                        range_of(krope_tree, krope_tree ? ((n - 1) * ld_krope_tree + Dr) * es : 0)};
+  if (any_overlap(outs, 2, ins, 2)) return DDTREE_ERR_INVALID_ARG;
+  RopeArgs a{};
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.Dr = Dr;
+  a.bf16 = dtype == DDTREE_BF16;
+  a.q_rope = q_rope;
+  a.krope_tree = krope_tree;
+  a.ld_krope_tree = ld_krope_tree;
+  a.positions = positions;
+  a.inv_freq = inv_freq;
+  hipError_t e = launch_rope_tree(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
+}
+
 }  // extern "C"

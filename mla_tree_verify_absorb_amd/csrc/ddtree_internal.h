@@ -66,6 +66,18 @@ struct CompactArgs {
 hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_verify_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_compact_kv(const CompactArgs& a, hipStream_t stream);
+// NeoX rotary embedding at tree positions
+constexpr int kMaxRopeDim = 512;
+struct RopeArgs {
+  int B, N, H, Dr;
+  bool bf16;
+  void* q_rope;              // [B, N, H, Dr] dense, or null
+  void* krope_tree;          // rows (b, i) at krope_tree + (b*N + i) * ld_krope_tree, or null
+  int64_t ld_krope_tree;     // elements
+  const int64_t* positions;  // [B, N]
+  const double* inv_freq;    // [Dr / 2]
+};
+hipError_t launch_rope_tree(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_build_tree(int B, int N, int D, int K, const int32_t* root_tokens, const int32_t* cand_tokens,
                              const float* cand_logp, int32_t* parents, int32_t* tokens, int32_t* depth, float* scores,
                              hipStream_t stream);

@@ -217,3 +217,26 @@ def test_build_tree_validation():
     assert btree(tok=None) == INVALID
     assert btree(par=A + 8192 + 64) == INVALID          # parents overlap cand_logp
     assert btree(dep=A + 16384 + 4) == INVALID          # depth overlaps parents
+
+
+# ---------------------------------------------------------------- rope_tree
+
+def rope(dtype=BF16, B=2, N=16, H=64, Dr=64, q=A, k=A + (1 << 24), ld=576, pos=A + (2 << 24), inv=A + (3 << 24)):
+    return dd.lib().ddtree_rope_tree(dtype, B, N, H, Dr, q, k, ld, pos, inv, None)
+
+
+def test_rope_tree_validation():
+    assert rope(dtype=9) == UNSUPPORTED
+    assert rope(Dr=63) == INVALID              # odd width
+    assert rope(Dr=0) == INVALID
+    assert rope(Dr=1024) == UNSUPPORTED
+    assert rope(N=257) == UNSUPPORTED
+    assert rope(H=0) == INVALID
+    assert rope(B=0) == OK
+    assert rope(q=None, k=None) == OK          # nothing to rotate
+    assert rope(pos=None) == INVALID
+    assert rope(inv=None) == INVALID
+    assert rope(ld=32) == INVALID              # key rows shorter than Dr
+    assert rope(q=A + 1) == INVALID            # not element aligned
+    assert rope(pos=A + 64) == INVALID         # positions overlap the rotated queries
+    assert rope(k=A + 4096) == INVALID         # keys overlap the queries

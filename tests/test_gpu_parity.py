@@ -456,3 +456,63 @@ def test_build_tree_feeds_build_mask():
     mask, mdepth, pos, ok = dd.ddtree_build_mask(parents)
     torch.cuda.synchronize()
     assert (ok.cpu() == 1).all() and torch.equal(mdepth.cpu(), depth.cpu())
+
+
+# ---------------------------------------------------------------- NeoX RoPE at tree positions
+
+def rope_expected(x_f32, pos, inv, dtype):
+    from oracle import rope_neox_ref
+    from synth import bf16_bits
+    y = rope_neox_ref(x_f32, pos, inv)
+    return bf16_bits(y.astype(np.float32)) if dtype == "bf16" else y.astype(np.float32)
+
+
+def max_ulp(a, b, dtype):
+    ia = a.view(np.uint16).astype(np.int64) if dtype == "bf16" else a.view(np.uint32).astype(np.int64)
+    ib = b.view(np.uint16).astype(np.int64) if dtype == "bf16" else b.view(np.uint32).astype(np.int64)
+    # same-sign values: the bit-pattern distance is the ulp distance
+    return int(np.abs(ia - ib).max()) if ia.size else 0
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_rope_tree_configs(k):
+    """Queries (all heads) and tree keys rotated at their build_mask positions: within 1 ulp of the
+    float64 oracle rounded to the storage type (the last bit may differ where the libraries' sin/cos do)."""
+    from oracle import rope_inv_freq
+    w, dw = config(k)
+    _, _, pos, _ = dw.build_mask()
+    inv = rope_inv_freq(w.Dr, 10000.0)
+    q = dw.q_rope.clone()
+    kt = dw.kv_tree.clone()
+    dd.ddtree_rope_tree(q, kt[..., w.Dl:], pos, torch.from_numpy(inv).cuda())
+    torch.cuda.synchronize()
+    p = pos.cpu().numpy()
+    exp_q = rope_expected(w.f32("q_rope"), p[:, :, None], inv, w.dtype)
+    exp_k = rope_expected(w.f32("kv_tree")[..., w.Dl:], p, inv, w.dtype)
+    got_q = from_dev_raw(q, w.dtype)
+    got_k = from_dev_raw(kt, w.dtype)[..., w.Dl:]
+    assert max_ulp(np.ascontiguousarray(got_q), exp_q, w.dtype) <= 1
+    assert max_ulp(np.ascontiguousarray(got_k), np.ascontiguousarray(exp_k), w.dtype) <= 1
+    # the latent part of the tree rows is untouched
+    assert np.array_equal(from_dev_raw(kt, w.dtype)[..., :w.Dl], host_rows(w, w.kv_tree)[..., :w.Dl])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_tree_queries_or_keys_alone_and_large_positions(dtype):
+    from oracle import rope_inv_freq
+    w = make_workload(B=2, N=9, H=3, Dl=8, Dr=128, dtype=dtype, std=1.0, scale=1.0, prefix=("list", [0, 5]),
+                      tree=("uniform",), seed=4)
+    dw = DevWorkload(w)
+    inv = rope_inv_freq(w.Dr, 500000.0)
+    pos = np.array([[0] * 9, list(range(2 ** 40, 2 ** 40 + 9))], np.int64)
+    q = dw.q_rope.clone()
+    dd.ddtree_rope_tree(q, None, torch.from_numpy(pos).cuda(), torch.from_numpy(inv).cuda())
+    kt = dw.kv_tree.clone()
+    dd.ddtree_rope_tree(None, kt[..., w.Dl:], torch.from_numpy(pos).cuda(), torch.from_numpy(inv).cuda())
+    torch.cuda.synchronize()
+    assert max_ulp(from_dev_raw(q, dtype), rope_expected(w.f32("q_rope"), pos[:, :, None], inv, dtype), dtype) <= 1
+    got_k = np.ascontiguousarray(from_dev_raw(kt, dtype)[..., w.Dl:])
+    exp_k = np.ascontiguousarray(rope_expected(w.f32("kv_tree")[..., w.Dl:], pos, inv, dtype))
+    assert max_ulp(got_k, exp_k, dtype) <= 1
+    # position 0 is the identity
+    assert np.array_equal(from_dev_raw(q, dtype)[0], host_rows(w, w.q_rope)[0])
