@@ -73,7 +73,7 @@ constexpr int MAXW = 8;                     // mask words per row (N <= 256)
 constexpr float kHeadroomLog2 = 100.0f;     // scores may exceed a row's reference by 2^100
 
 static_assert(KT * R_ROW == NWAVES * 1024, "rotary region must split into one 1 KB load per wave");
-static_assert(LOADS_PER_WAVE == 9, "the tile loop's vmcnt wait assumes 9 loads per wave per tile");
+static_assert(LOADS_PER_WAVE == 9, "the copies are spread over the first 27 S^T MFMAs (one every third)");
 
 // LDS layout of a tile.  Latent rows: key k at k * 1024, its 16-byte chunk p at
 // 16 * (p >> 4) + ((p & 15) ^ swz(k)).  gfx950 serves 16-byte reads from 64
@@ -97,36 +97,6 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
-struct TileSrc {
-  const uint16_t* c;   // latent rows of the tile's first key
-  const uint16_t* r;   // rotary rows of the tile's first key
-  int ldc, ldr;        // row strides (elements)
-  int count;           // valid keys in this tile (1..32)
-};
-
-__device__ __forceinline__ TileSrc tile_source(const AttnArgs& a, int b, int64_t p0, int64_t L, int n_pt, int t) {
-  TileSrc s;
-  if (t < n_pt) {
-    const int64_t row0 = p0 + (int64_t)t * KT;
-    s.c = static_cast<const uint16_t*>(a.ckv) + row0 * a.ld_ckv;
-    s.r = static_cast<const uint16_t*>(a.krope) + row0 * a.ld_krope;
-    s.ldc = (int)a.ld_ckv;
-    s.ldr = (int)a.ld_krope;
-    const int64_t rem = L - (int64_t)t * KT;
-    s.count = rem < KT ? (int)rem : KT;
-  } else {
-    const int node0 = (t - n_pt) * KT;
-    const int64_t row0 = (int64_t)b * a.N + node0;
-    s.c = static_cast<const uint16_t*>(a.ckv_tree) + row0 * a.ld_ckv_tree;
-    s.r = static_cast<const uint16_t*>(a.krope_tree) + row0 * a.ld_krope_tree;
-    s.ldc = (int)a.ld_ckv_tree;
-    s.ldr = (int)a.ld_krope_tree;
-    const int rem = a.N - node0;
-    s.count = rem < KT ? rem : KT;
-  }
-  return s;
-}
-
 // One direct-to-LDS 16-byte load per lane: LDS[lds_base + 16 * lane] <- gbase[voff].
 // Written as inline asm so that the compiler does not treat it as an LDS store
 // and serialise every later LDS read behind it; completion is tracked by the
@@ -144,44 +114,22 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gbase, 
       : "memory");
 }
 
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-}
+// Wait for every tile copy this wave has issued.
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Issue this wave's direct-to-LDS 16-byte loads of one tile (layout above).
-// Wave w loads latent rows w, w + 4, ..., w + 28 (one 64-lane load each; lane =
-// physical chunk, so the lane fetches global chunk lane ^ swz(key)), and the
-// 1 KB of the rotary region holding keys 8 w .. 8 w + 7 (pair rows 4 w ..
-// 4 w + 3; lane = 16 * pair row + physical chunk).  Keys past the tile's valid
-// count re-read its last valid row (masked later).
-__device__ __forceinline__ void issue_tile_loads(const TileSrc& s, uint32_t lds_buf, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < C_LOADS_PER_WAVE; ++i) {
-    const int key = wave + NWAVES * i;                    // wave-uniform
-    const int kc = min(key, s.count - 1);
-    const uint16_t* row = s.c + (int64_t)kc * s.ldc;      // scalar address
-    // lane offsets are recomputed per copy (opaque to the optimiser) instead of
-    // being kept in, or spilled from, registers across the tile loop
-    lds_dma16(lds_buf + key * C_ROW, row, (uint32_t)(opaque(lane << 4) ^ (swz(key) << 4)));
-  }
-  {
-    const int pr = wave * 4 + (opaque(lane) >> 4);        // pair row
-    const int logical = (lane & 15) ^ (pr & 7);
-    const int key = 2 * pr + (logical >> 3);
-    const int kc = min(key, s.count - 1);
-    lds_dma16(lds_buf + R_OFF + wave * 1024, s.r, (uint32_t)(kc * s.ldr + (logical & 7) * 8) * 2u);
-  }
-}
-
-// Copies of one tile spread through the S^T MFMA stream.  A CopyPlan holds the
-// tile's row bases and strides (scalar) and its valid key count; copy i < 8
-// loads latent key wave + 4 i (clamped to the last valid key), copy 8 the
-// wave's 1 KB of rotary pair rows, in the LDS layout of issue_tile_loads.  The
-// swizzle of key wave + 4 i is 2 wave + 8 (i & 1) + ((i >> 1) & 1), so the
-// lane's chunk offset (lane ^ swz) * 16 is lw[i & 1] ^ (16 if i & 2) with
-// lw0 = 16 lane ^ 32 wave and lw1 = lw0 ^ 128.  The rotary copy of lane
-// (pair row 4 wave + lane / 16) reads key rkey (clamped), 16-byte piece rpiece.
+// The direct-to-LDS copies of one tile (LDS layout above), 9 per wave.  Copy
+// i < 8 loads latent key wave + 4 i with one 64-lane load (lane = physical
+// chunk, so the lane fetches global chunk lane ^ swz(key)); copy 8 loads the
+// 1 KB of the rotary region holding keys 8 wave .. 8 wave + 7 (pair rows
+// 4 wave .. 4 wave + 3; lane = 16 * pair row + physical chunk).  Keys past the
+// tile's valid count re-read its last valid row (masked later).  A CopyPlan
+// holds the tile's row bases and strides (scalar) and its valid key count.
+// The swizzle of key wave + 4 i is 2 wave + 8 (i & 1) + ((i >> 1) & 1), so
+// the lane's chunk offset (lane ^ swz) * 16 is lw[i & 1] ^ (16 if i & 2),
+// with lw0 = 16 lane ^ 32 wave and lw1 = lw0 ^ 128.  The rotary copy of a lane
+// reads key rkey (clamped), 16-byte piece rpiece.  Lane values go through
+// opaque() so that they are recomputed per copy instead of being kept in, or
+// spilled from, registers across the tile loop.
 struct CopyLanes {
   uint32_t lw0, lw1;   // latent chunk offsets for even / odd i
   int rkey;            // rotary: the lane's key within the tile
@@ -432,7 +380,11 @@ verify_attn_bf16_kernel(AttnArgs a) {
   // ---- prologue: tile t0 in flight ----
   bf16x8 pb[2] = {bf16x8{}, bf16x8{}};
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing of the compiler's pending inside the loop
-  if (t0 < t1) issue_tile_loads(tile_source(a, b, p0, L, n_pt, t0), lds0, wave, lane);
+  if (t0 < t1) {
+    const CopyPlan cp0 = copy_plan(a, b, p0, L, n_pt, t0);
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) issue_copy(cp0, clanes, lds0, wave, i);
+  }
   int slot = 2;                          // ring slot of tile t (t0 - 1: none)
 
   for (int t = t0 - 1; t < t1; ++t) {
@@ -442,7 +394,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
     f32x16 sn;                    // S^T, then exponents, of tile tn
     float c, m, m_abs;
     if (tn < t1) {
-      wait_vmcnt_le(0);           // this wave's copies of tile tn have landed
+      wait_copies();              // this wave's copies of tile tn have landed
       __syncthreads();            // ... and every wave's; every wave is done with tile t - 1
 
       // ---- S^T[key][row] = K . Q^T over 576 dims for tile tn; K-fragment reads
@@ -593,7 +545,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
     slot = slot_n;
   }
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");   // last O^T MFMA -> AGPR reads / rewrites
-  wait_vmcnt_le(0);   // the repeated copy of the last tile (if any) has landed
+  wait_copies();   // the repeated copy of the last tile (if any) has landed
 
   // rare: a score beyond the headroom anywhere in the workgroup -> one more pass
   if (!__syncthreads_or(overflow ? 1 : 0)) break;
