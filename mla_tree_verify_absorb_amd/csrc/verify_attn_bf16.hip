@@ -76,15 +76,19 @@ static_assert(KT * R_ROW == NWAVES * 1024, "rotary region must split into one 1 
 static_assert(LOADS_PER_WAVE == 9, "the copies are spread over the first 27 S^T MFMAs (one every third)");
 
 // LDS layout of a tile.  Latent rows: key k at k * 1024, its 16-byte chunk p at
-// 16 * (p >> 4) + ((p & 15) ^ swz(k)).  gfx950 serves 16-byte reads from 64
-// banks, 16 lanes at a time: the key-fragment read (16 consecutive keys, one
-// chunk) needs swz to be a bijection on k & 15, and the transpose read (4
-// consecutive keys, 2 adjacent chunks) needs (swz(k) >> 1) distinct over the 4
-// keys; swz(k) = ((k & 7) << 1) | ((k >> 3) & 1) does both.  The rotary rows
+// 16 * (p >> 4) + ((p & 15) ^ swz(k)).  gfx950's LDS has 64 banks of 4 bytes.
+// The key-fragment read (ds_read_b128) is served 16 lanes at a time: 16
+// consecutive keys, one chunk, so swz must be a bijection on k & 15.  The
+// transpose read (ds_read_b64_tr_b16) is served 32 lanes at a time: 4 keys of
+// an aligned group of 4, each with 4 consecutive chunks of an aligned group of
+// 4 (both 8-byte halves), so the 4 keys must land in 4 different chunk
+// groups: (swz(k) >> 2) distinct over k & 3 (bank-conflict counters confirm
+// that pass size).  swz(k) = ((k & 3) << 2) | ((k >> 2) & 3) does both, and
+// swz(k + 8) = swz(k) ^ 2, swz(k + 16) = swz(k).  The rotary rows
 // (8 chunks) are stored in pairs: keys 2 j and 2 j + 1 share the 256-byte row j,
 // logical chunk (k & 1) * 8 + c at ((k & 1) * 8 + c) ^ (j & 7), which again
 // spreads 16 consecutive keys over all 64 banks.
-__device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+__device__ __forceinline__ int swz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
 __device__ __forceinline__ int pair_chunk(int key, int c) { return (((key & 1) << 3) | c) ^ ((key >> 1) & 7); }
 
 // Hides a value from the optimiser (no code is emitted).
@@ -124,14 +128,14 @@ __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)
 // 4 wave .. 4 wave + 3; lane = 16 * pair row + physical chunk).  Keys past the
 // tile's valid count re-read its last valid row (masked later).  A CopyPlan
 // holds the tile's row bases and strides (scalar) and its valid key count.
-// The swizzle of key wave + 4 i is 2 wave + 8 (i & 1) + ((i >> 1) & 1), so
-// the lane's chunk offset (lane ^ swz) * 16 is lw[i & 1] ^ (16 if i & 2),
-// with lw0 = 16 lane ^ 32 wave and lw1 = lw0 ^ 128.  The rotary copy of a lane
+// The swizzle of key wave + 4 i is 4 wave + (i & 3), so the lane's chunk
+// offset (lane ^ swz) * 16 is lw ^ 16 (i & 3), with lw = 16 lane ^ 64 wave
+// (one v_xad_u32 per copy).  The rotary copy of a lane
 // reads key rkey (clamped), 16-byte piece rpiece.  Lane values go through
 // opaque() so that they are recomputed per copy instead of being kept in, or
 // spilled from, registers across the tile loop.
 struct CopyLanes {
-  uint32_t lw0, lw1;   // latent chunk offsets for even / odd i
+  uint32_t lw;         // latent chunk offset of copy 0
   int rkey;            // rotary: the lane's key within the tile
   uint32_t rpiece;     // rotary: byte offset of the lane's 16 bytes within the key's rotary row
 };
@@ -169,8 +173,7 @@ __device__ __forceinline__ void issue_copy(const CopyPlan& q, const CopyLanes& c
   if (i < C_LOADS_PER_WAVE) {
     const int key = wave + NWAVES * i;
     const uint32_t kc = (uint32_t)min(key, q.count - 1);
-    const uint32_t lw = (i & 1) ? opaque(cl.lw1) : opaque(cl.lw0);
-    lds_dma16(lds_buf + key * C_ROW, q.c, (lw ^ ((i & 2) ? 16u : 0u)) + kc * q.cstride);
+    lds_dma16(lds_buf + key * C_ROW, q.c, (opaque(cl.lw) ^ (uint32_t)((i & 3) << 4)) + kc * q.cstride);
   } else {
     const uint32_t kc = (uint32_t)min(opaque(cl.rkey), q.count - 1);
     lds_dma16(lds_buf + R_OFF + wave * 1024, q.r, kc * q.rstride + opaque(cl.rpiece));
@@ -184,11 +187,11 @@ __device__ __forceinline__ int kaddr(int kbase, int s) { return (kbase ^ ((s & 7
 // V^T fragment of 16-key step ks and 32-dim block db: two transpose reads of
 // 4 keys each (keys 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3).  voff holds
 // the lane's row and swizzled chunk for db = 0, first read; db & 3 and the +8
-// keys (whose swizzle differs in bit 0) enter by XOR, db >> 2 and ks by offset.
+// keys (whose swizzle differs in bit 1) enter by XOR, db >> 2 and ks by offset.
 __device__ __forceinline__ bf16x8 load_vt(const unsigned char* buf, int voff, int ks, int db) {
   const int o = (voff ^ ((db & 3) << 6)) + (db >> 2) * 256 + ks * 16 * C_ROW;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + o));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + (o ^ 16) + 8 * C_ROW));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + (o ^ 32) + 8 * C_ROW));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -338,8 +341,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)s_kv;   // LDS byte address of the ring
   CopyLanes clanes;
   {
-    clanes.lw0 = (uint32_t)((lane << 4) ^ (wave << 5));
-    clanes.lw1 = clanes.lw0 ^ 128u;
+    clanes.lw = (uint32_t)((lane << 4) ^ (wave << 6));
     const int pr = wave * 4 + (lane >> 4);
     const int logical = (lane & 15) ^ (pr & 7);
     clanes.rkey = 2 * pr + (logical >> 3);
