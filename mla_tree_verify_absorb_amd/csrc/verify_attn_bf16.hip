@@ -186,12 +186,14 @@ __device__ __forceinline__ int kaddr(int kbase, int s) { return (kbase ^ ((s & 7
 
 // V^T fragment of 16-key step ks and 32-dim block db: two transpose reads of
 // 4 keys each (keys 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3).  voff holds
-// the lane's row and swizzled chunk for db = 0, first read; db & 3 and the +8
-// keys (whose swizzle differs in bit 1) enter by XOR, db >> 2 and ks by offset.
-__device__ __forceinline__ bf16x8 load_vt(const unsigned char* buf, int voff, int ks, int db) {
-  const int o = (voff ^ ((db & 3) << 6)) + (db >> 2) * 256 + ks * 16 * C_ROW;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + o));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + (o ^ 32) + 8 * C_ROW));
+// the lane's row and swizzled chunk for db = 0, first read, and voff_hi the
+// same for the second read (8 keys on, whose swizzle differs in bit 1:
+// (voff ^ 32) + 8 rows); db & 3 enters by XOR, db >> 2 and ks by offset, so
+// both reads of every step are a per-tile base plus an immediate.
+__device__ __forceinline__ bf16x8 load_vt(const unsigned char* buf, int voff, int voff_hi, int ks, int db) {
+  const int add = (db >> 2) * 256 + ks * 16 * C_ROW;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + (voff ^ ((db & 3) << 6)) + add));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + (voff_hi ^ ((db & 3) << 6)) + add));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -338,6 +340,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
     const int vkey = 4 * g + rr;
     voff = vkey * C_ROW + (((2 * (G & 1) + (cc >> 1)) ^ swz(vkey)) << 4) + (cc & 1) * 8;
   }
+  const int voff_hi = (voff ^ 32) + 8 * C_ROW;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)s_kv;   // LDS byte address of the ring
   CopyLanes clanes;
   {
@@ -508,12 +511,12 @@ verify_attn_bf16_kernel(AttnArgs a) {
       constexpr int NST = 2 * (DL / 32);
       bf16x8 vring[VRING];
 #pragma unroll
-      for (int st = 0; st < VRING; ++st) vring[st] = load_vt(buf, voff, st / (DL / 32), st % (DL / 32));
+      for (int st = 0; st < VRING; ++st) vring[st] = load_vt(buf, voff, voff_hi, st / (DL / 32), st % (DL / 32));
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const int ks = st / (DL / 32), db = st % (DL / 32);
         const bf16x8 vf = vring[st % VRING];
-        if (st + VRING < NST) vring[st % VRING] = load_vt(buf, voff, (st + VRING) / (DL / 32), (st + VRING) % (DL / 32));
+        if (st + VRING < NST) vring[st % VRING] = load_vt(buf, voff, voff_hi, (st + VRING) / (DL / 32), (st + VRING) % (DL / 32));
         if (st == 0)
           mfma_o_first(oacc[db], vf, pb[ks]);
         else
