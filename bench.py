@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5, help="workload number (3, 4 or 5); 5 is the headline")
-    ap.add_argument("--splits", type=int, default=0, help="KV splits (0 = library's automatic choice)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="uniform KV splits (0 = the library's automatic schedule)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times (HBM counter calibration)")
@@ -221,6 +222,7 @@ def main():
     max_len = int(w.prefix_lens.max())
     code = dd.DDTREE_BF16 if w.dtype == "bf16" else dd.DDTREE_F32
     splits = args.splits or dd.ddtree_verify_attn_auto_splits(code, w.B, w.N, w.H, w.Dl, w.Dr, max_len)
+    schedule = "band" if splits == 0 else f"uniform-{splits}"
     ws_bytes = dd.ddtree_verify_attn_workspace_size(code, w.B, w.N, w.H, w.Dl, w.Dr, max_len, splits)
     workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     W = (w.N + 31) // 32
@@ -287,7 +289,7 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": CONFIGS[args.config]["name"], "batch": w.B, "tree_nodes": w.N, "heads": w.H,
                    "kv_lora": w.Dl, "rope_dim": w.Dr, "prefix_len_max": max_len,
-                   "prefix_len_total": int(w.prefix_lens.sum()), "vocab": w.V, "kv_splits": splits},
+                   "prefix_len_total": int(w.prefix_lens.sum()), "vocab": w.V, "schedule": schedule},
         "verify_steps_per_s": round(1e3 / step_ms, 2),
         "attn_tflops": round(attn_tflops, 2),
         "attn_hbm_gbps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),

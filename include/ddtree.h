@@ -116,12 +116,22 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *   krope_tree, ld_krope_tree  device tree-node rotary keys, same indexing
  *   mask             device uint32 [B, N, ceil(N/32)] from ddtree_build_mask
  *   softmax_scale    finite scale applied to q.k (e.g. 1/sqrt(qk head dim))
- *   num_splits       number of KV splits per query block, 0 = automatic
+ *   num_splits       0 = automatic schedule; S > 0 = S uniform KV splits per
+ *                    block of 128 query rows (flash-decoding).  Automatic: when
+ *                    ceil(N*H/128) is a multiple of 32, the band schedule: a
+ *                    request's 128-row blocks are grouped 32 at a time, the
+ *                    groups' KV tiles laid end to end and cut into 8 equal
+ *                    ranges, one per XCD (32 workgroups each), so that every CU
+ *                    carries the same work however ragged the prefix lengths;
+ *                    otherwise uniform splits (ddtree_verify_attn_auto_splits)
  *   o                device float32 [B, N, H, Dl]
  *   lse              device float32 [B, N, H] (natural log)
  *   workspace        device scratch of workspace_bytes >=
  *                    ddtree_verify_attn_workspace_size(...) with the same shape
- *                    and num_splits (may be NULL when that size is 0)
+ *                    and num_splits (may be NULL when that size is 0); S
+ *                    splits take S*B*N*H*(Dl+1) floats, the band schedule
+ *                    512*128*(Dl+1) floats plus 128 bytes (134.5 MB)
+ *                    whatever B
  * bf16 inputs need 16-byte aligned base pointers and row strides that are
  * multiples of 8 elements (INVALID_ARG otherwise) and at most 2^24 elements
  * (UNSUPPORTED otherwise).  Requests whose tree_ok is 0 give undefined o/lse.
@@ -129,7 +139,8 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
 size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                          int64_t max_prefix_len, int32_t num_splits);
 
-/* The KV split count that num_splits = 0 selects for this shape (>= 1). */
+/* What num_splits = 0 selects for this shape: 0 for the band schedule, else the
+ * uniform KV split count (>= 1). */
 int32_t ddtree_verify_attn_auto_splits(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                        int64_t max_prefix_len);
 

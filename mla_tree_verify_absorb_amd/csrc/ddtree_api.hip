@@ -66,13 +66,28 @@ int auto_splits(int dtype, int B, int N, int H, int64_t max_prefix_len) {
   return (int)(s < 1 ? 1 : s);
 }
 
+// The automatic schedule is the band schedule whenever a request's row blocks
+// come in whole bands of kBandRowBlocks; 0 stands for it.
+bool band_schedule_applies(int dtype, int N, int H) {
+  return dtype == DDTREE_BF16 && ceil_div((int64_t)N * H, kRowsPerBlock) % kBandRowBlocks == 0;
+}
+
+int auto_schedule(int dtype, int B, int N, int H, int64_t max_prefix_len) {
+  if (band_schedule_applies(dtype, N, H)) return 0;
+  return auto_splits(dtype, B, N, H, max_prefix_len);
+}
+
+// Uniform split count (>= 1), or 0 for the band schedule.
 int resolve_splits(int dtype, int B, int N, int H, int64_t max_prefix_len, int num_splits) {
   if (dtype != DDTREE_BF16) return 1;
-  return num_splits > 0 ? num_splits : auto_splits(dtype, B, N, H, max_prefix_len);
+  return num_splits > 0 ? num_splits : auto_schedule(dtype, B, N, H, max_prefix_len);
 }
 
 size_t workspace_bytes_for(int dtype, int B, int N, int H, int Dl, int splits) {
-  if (dtype != DDTREE_BF16 || splits <= 1) return 0;
+  if (dtype != DDTREE_BF16) return 0;
+  if (splits == 0)
+    return (size_t)kBandPartSlots * kRowsPerBlock * (uint64_t)(Dl + 1) * sizeof(float) + kBandWindows * 4 * sizeof(int);
+  if (splits == 1) return 0;
   const uint64_t rows = (uint64_t)B * N * H;
   return (size_t)(splits * rows * (uint64_t)(Dl + 1) * sizeof(float));
 }
@@ -113,7 +128,8 @@ int32_t ddtree_verify_attn_auto_splits(int32_t dtype, int32_t B, int32_t N, int3
                                        int64_t max_prefix_len) {
   (void)Dl;
   (void)Dr;
-  return auto_splits(dtype, B, N, H, max_prefix_len);
+  if (B <= 0 || N <= 0 || H <= 0) return 1;
+  return auto_schedule(dtype, B, N, H, max_prefix_len);
 }
 
 size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
@@ -195,20 +211,27 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   a.ld_krope_tree = ld_krope_tree;
   a.mask = mask;
   a.scale = softmax_scale;
-  a.splits = splits;
+  a.splits = splits > 0 ? splits : 1;
+  a.balanced = splits == 0 ? 1 : 0;
   a.o = o;
   a.lse = lse;
   a.part_o = nullptr;
   a.part_lse = nullptr;
+  a.band_edges = nullptr;
   if (splits > 1) {
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = a.part_o + (uint64_t)splits * rows * Dl;
+  } else if (splits == 0) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (uint64_t)kBandPartSlots * kRowsPerBlock * Dl;
+    a.band_edges = reinterpret_cast<int*>(a.part_lse + (uint64_t)kBandPartSlots * kRowsPerBlock);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == DDTREE_BF16) {
     e = launch_verify_attn_bf16(a, s);
     if (e == hipSuccess && splits > 1) e = launch_attn_combine(a, s);
+    if (e == hipSuccess && splits == 0) e = launch_attn_band_combine(a, s);
   } else {
     e = launch_verify_attn_f32(a, s);
   }

@@ -31,11 +31,15 @@ struct AttnArgs {
   int64_t ld_krope_tree;
   const uint32_t* mask;
   float scale;
-  int splits;          // >= 1
+  int splits;          // >= 1 (uniform schedule)
+  int balanced;        // 1: band schedule (row blocks per request a multiple of kBandRowBlocks)
   float* o;
   float* lse;
-  float* part_o;       // [splits][B*N*H][Dl]  (splits > 1)
-  float* part_lse;     // [splits][B*N*H]      (splits > 1)
+  // uniform schedule, splits > 1: part_o [splits][B*N*H][Dl], part_lse [splits][B*N*H]
+  // band schedule: part_o [kBandPartSlots][kRowsPerBlock][Dl], part_lse [kBandPartSlots][kRowsPerBlock]
+  float* part_o;
+  float* part_lse;
+  int* band_edges;     // band schedule: [kBandWindows][4] cut descriptors (after part_lse)
 };
 
 // bf16 MFMA kernel for (Dl, Dr) = (512, 64)
@@ -43,6 +47,12 @@ constexpr int kMfmaDl = 512;
 constexpr int kMfmaDr = 64;
 constexpr int kRowsPerBlock = 128;   // query rows (node, head) per workgroup
 constexpr int kKeysPerTile = 32;     // latent KV rows per LDS tile
+// Band schedule: 32 row blocks of one request (one per CU of an XCD) form a band;
+// the bands' KV tile columns are cut into 8 equal windows, one per XCD, and each
+// workgroup of a window keeps at most one piece at each window edge.
+constexpr int kBandRowBlocks = 32;
+constexpr int kBandWindows = 8;
+constexpr int kBandPartSlots = 2 * kBandWindows * kBandRowBlocks;
 constexpr int64_t kMaxBf16RowStride = int64_t(1) << 24;   // elements; keeps tile row offsets in 32 bits
 
 // KV-cache compaction (byte addressing; strides in bytes)
@@ -82,5 +92,6 @@ hipError_t launch_build_tree(int B, int N, int D, int K, const int32_t* root_tok
                              const float* cand_logp, int32_t* parents, int32_t* tokens, int32_t* depth, float* scores,
                              hipStream_t stream);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_band_combine(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace ddtree

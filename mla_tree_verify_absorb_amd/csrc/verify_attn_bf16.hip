@@ -52,6 +52,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -71,6 +72,7 @@ constexpr int C_LOADS_PER_WAVE = KT / NWAVES;   // 8 latent rows (1 KB each) per
 constexpr int LOADS_PER_WAVE = C_LOADS_PER_WAVE + 1;  // + one 1 KB slice of the rotary region
 constexpr int MAXW = 8;                     // mask words per row (N <= 256)
 constexpr float kHeadroomLog2 = 100.0f;     // scores may exceed a row's reference by 2^100
+constexpr bf16x2 kBf16Ones = {(__bf16)1.0f, (__bf16)1.0f};
 
 static_assert(KT * R_ROW == NWAVES * 1024, "rotary region must split into one 1 KB load per wave");
 static_assert(LOADS_PER_WAVE == 9, "the copies are spread over the first 27 S^T MFMAs (one every third)");
@@ -252,6 +254,159 @@ __device__ __forceinline__ int xcd_local_item(int block, int total) {
   return x * base + min(x, extra) + k;
 }
 
+// ---- band schedule ----------------------------------------------------------
+// Used when a request's row blocks come in whole groups of kBandRowBlocks (32,
+// the CUs of one XCD).  Such a group is a band: its row blocks all stream the
+// request's KV, Tb = ceil(L_b / 32) + ceil(N / 32) tile columns (a row block
+// that sees fewer tree tiles skips the excess).  The bands are laid end to end
+// in (request, band) order and their columns cut into kBandWindows equal
+// windows, one per XCD.  Workgroup (window x, slot j) takes row block j of every
+// band piece in window x, so every CU carries the same number of tiles however
+// ragged the prefixes are, and the 32 workgroups of an XCD walk the same
+// columns in step (one KV stream per L2).  A band cut by a window edge leaves
+// one partial (o, lse) per window it touches, at a slot fixed by (window, slot,
+// head or tail of the window); the band combine kernel merges them.
+
+__device__ __forceinline__ int64_t request_len(const int64_t* off, int b) {
+  const int64_t L = off[b + 1] - off[b];
+  return L > 0 ? L : 0;
+}
+__device__ __forceinline__ int band_tiles(const int64_t* off, int b, int ntt) {
+  return (int)((request_len(off, b) + KT - 1) / KT) + ntt;
+}
+
+// Total band columns over all requests (same value in every lane).
+__device__ int64_t band_columns_total(const int64_t* off, int B, int nb, int ntt) {
+  const int lane = threadIdx.x & 63;
+  long long sum = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    long long c = b < B ? (long long)nb * band_tiles(off, b, ntt) : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
+    sum += c;
+  }
+  return sum;
+}
+
+// The first request whose columns end after column X, and in S the column its
+// first band starts at; B (with S = the total) if X is past the end.
+__device__ int band_find(const int64_t* off, int B, int nb, int ntt, int64_t X, int64_t& S) {
+  const int lane = threadIdx.x & 63;
+  long long carry = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const long long c = b < B ? (long long)nb * band_tiles(off, b, ntt) : 0;
+    long long inc = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long y = __shfl_up(inc, d);
+      if (lane >= d) inc += y;
+    }
+    const unsigned long long hit = __ballot(b < B && carry + inc > X);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      S = carry + __shfl(inc - c, l);
+      return b0 + l;
+    }
+    carry += __shfl(inc, 63);
+  }
+  S = carry;
+  return B;
+}
+
+__device__ __forceinline__ int64_t window_edge(int64_t C, int x) { return C * x / kBandWindows; }
+
+// Partial slot of workgroup (window, slot): the band cut at the window's start
+// (head) or the one cut at its end (tail).  A window inside one band has only a head.
+__device__ __forceinline__ int band_part_slot(int win, int slot, bool head) {
+  return (win * kBandRowBlocks + slot) * 2 + (head ? 0 : 1);
+}
+
+struct PieceCursor {
+  int b, k;          // request, band within the request
+  int Tb;            // columns of request b's bands
+  int nb, ntt;       // bands per request, tree tiles of a band
+  int win, slot;     // window (XCD) and row block within each band
+  int64_t S;         // first column of request b
+  int64_t X0, X1;    // the window's columns
+};
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The cursor read back from LDS, made wave-uniform (scalar registers).
+__device__ __forceinline__ PieceCursor uniform_cursor(const PieceCursor& v) {
+  PieceCursor c;
+  c.b = __builtin_amdgcn_readfirstlane(v.b);
+  c.k = __builtin_amdgcn_readfirstlane(v.k);
+  c.Tb = __builtin_amdgcn_readfirstlane(v.Tb);
+  c.nb = __builtin_amdgcn_readfirstlane(v.nb);
+  c.ntt = __builtin_amdgcn_readfirstlane(v.ntt);
+  c.win = __builtin_amdgcn_readfirstlane(v.win);
+  c.slot = __builtin_amdgcn_readfirstlane(v.slot);
+  c.S = uniform64(v.S);
+  c.X0 = uniform64(v.X0);
+  c.X1 = uniform64(v.X1);
+  return c;
+}
+
+__device__ PieceCursor band_cursor_start(const AttnArgs& a, int n_rb, int block) {
+  PieceCursor c;
+  c.win = block % kBandWindows;
+  c.slot = block / kBandWindows;
+  c.nb = n_rb / kBandRowBlocks;
+  c.ntt = (a.N + KT - 1) / KT;
+  const int64_t C = uniform64(band_columns_total(a.prefix_offsets, a.B, c.nb, c.ntt));
+  c.X0 = window_edge(C, c.win);
+  c.X1 = window_edge(C, c.win + 1);
+  int64_t S;
+  c.b = __builtin_amdgcn_readfirstlane(band_find(a.prefix_offsets, a.B, c.nb, c.ntt, c.X0, S));
+  c.S = uniform64(S);
+  c.k = 0;
+  c.Tb = 1;
+  if (c.b < a.B) {
+    c.Tb = band_tiles(a.prefix_offsets, c.b, c.ntt);
+    c.k = (int)((c.X0 - c.S) / c.Tb);
+  }
+  // Workgroup (window x > 0, slot 0) describes edge x for the combine kernel:
+  // {cut here first, request, band, windows holding head pieces}.  The band
+  // holding column X_x is cut first at x when it starts strictly inside
+  // window x - 1 (at or after X_{x-1}, before X_x).
+  if (c.slot == 0 && c.win > 0 && threadIdx.x == 0) {
+    int4 d = make_int4(0, 0, 0, 0);
+    if (c.b < a.B) {
+      const int64_t bs = c.S + (int64_t)c.k * c.Tb, be = bs + c.Tb;
+      if (bs != c.X0 && window_edge(C, c.win - 1) <= bs) {
+        unsigned heads = 0;
+        for (int x = c.win; x < kBandWindows && window_edge(C, x) < be; ++x)
+          if (window_edge(C, x) < window_edge(C, x + 1)) heads |= 1u << x;
+        d = make_int4(1, c.b, c.k, (int)heads);
+      }
+    }
+    reinterpret_cast<int4*>(a.band_edges)[c.win] = d;
+  }
+  return c;
+}
+
+// The next piece's first band column bs; false when the window is done.
+__device__ __forceinline__ bool band_cursor_piece(const AttnArgs& a, const PieceCursor& c, int64_t& bs) {
+  if (c.X0 >= c.X1 || c.b >= a.B) return false;
+  bs = c.S + (int64_t)c.k * c.Tb;
+  return bs < c.X1;
+}
+
+__device__ __forceinline__ void band_cursor_next(const AttnArgs& a, PieceCursor& c) {
+  if (++c.k < c.nb) return;
+  c.k = 0;
+  c.S += (int64_t)c.nb * c.Tb;
+  if (++c.b < a.B) c.Tb = band_tiles(a.prefix_offsets, c.b, c.ntt);
+}
+
 constexpr int KRING = 4;   // K-fragment reads in flight ahead of the S^T MFMAs
 constexpr int QREG = DL / 16 - 4;   // latent query k-steps held in VGPRs; the last 4 are staged in LDS
 static_assert(DL / 16 - QREG == DR / 16, "the staged latent queries use the rotary pair-row layout");
@@ -263,6 +418,9 @@ verify_attn_bf16_kernel(AttnArgs a) {
   __shared__ uint32_t s_mask[ROWS][MAXW];
   // queries of the last QREG_LDS latent k-steps (part 0) and the rotary ones (part 1), swizzled pair rows
   __shared__ __attribute__((aligned(16))) unsigned char s_qx[2 * ROWS * R_ROW];
+  __shared__ PieceCursor s_cur;
+  // second bf16 term of P of one tile, per lane, in the lane's B-operand layout
+  __shared__ __attribute__((aligned(16))) unsigned char s_plo[NWAVES * 64 * 32];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -270,24 +428,90 @@ verify_attn_bf16_kernel(AttnArgs a) {
   const int g = lane >> 5;          // which 8-wide k half of an MFMA operand
   const int lr = lane & 31;         // row within the wave's 32 rows
 
-  // ---- work item: (request, row block, split) ----
+  // ---- LDS addresses (lane constants) ----
+  const int kbase = lr * C_ROW + ((g ^ swz(lr)) << 4);   // K fragment, k-step 0
+  // V^T fragment (A of O^T) by transpose read.  Lane = 16 G + 4 rr + cc reads key
+  // 16 ks + 4 g + rr (+8 for the second read), dims 32 db + 16 (G & 1) + 4 cc .. +3,
+  // i.e. logical chunk 4 db + 2 (G & 1) + (cc >> 1), byte 8 (cc & 1) in it.
+  int voff;
+  {
+    const int G = lane >> 4;
+    const int rr = (lane >> 2) & 3;
+    const int cc = lane & 3;
+    const int vkey = 4 * g + rr;
+    voff = vkey * C_ROW + (((2 * (G & 1) + (cc >> 1)) ^ swz(vkey)) << 4) + (cc & 1) * 8;
+  }
+  const int voff_hi = (voff ^ 32) + 8 * C_ROW;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)s_kv;   // LDS byte address of the ring
+  CopyLanes clanes;
+  {
+    clanes.lw = (uint32_t)((lane << 4) ^ (wave << 6));
+    const int pr = wave * 4 + (lane >> 4);
+    const int logical = (lane & 15) ^ (pr & 7);
+    clanes.rkey = 2 * pr + (logical >> 3);
+    clanes.rpiece = (uint32_t)((logical & 7) * 16);
+  }
+
+  // ---- the workgroup's pieces of work: (request, row block, tile range, destination) ----
   const int n_rows = a.N * a.H;
   const int n_rb = (n_rows + ROWS - 1) / ROWS;
-  int item = xcd_local_item(blockIdx.x, gridDim.x);
-  const int split = item % a.splits;
-  item /= a.splits;
-  const int rb = item % n_rb;
-  const int b = item / n_rb;
+  const int64_t total_rows = (int64_t)a.B * n_rows;
+  // The band cursor lives in LDS between pieces, so that none of it is held in
+  // registers across the tile loop.
+  if (a.balanced) {
+    const PieceCursor c = band_cursor_start(a, n_rb, blockIdx.x);
+    if (tid == 0) s_cur = c;
+  }
+  bool single_done = false;
 
-  const int64_t p0 = a.prefix_offsets[b];
-  int64_t L = a.prefix_offsets[b + 1] - p0;
-  if (L < 0) L = 0;
-  const int n_pt = (int)((L + KT - 1) / KT);
-  const int last_row = min(n_rows - 1, rb * ROWS + ROWS - 1);
-  const int n_tt = (last_row / a.H) / KT + 1;     // tree tiles that any row here can see
-  const int T = n_pt + n_tt;
-  const int t0 = (int)((int64_t)split * T / a.splits);
-  const int t1 = (int)((int64_t)(split + 1) * T / a.splits);
+  for (;;) {
+  __syncthreads();   // the cursor is visible; every wave is done with the previous piece's LDS
+  int b, rb, t0, t1;
+  bool to_part;                   // partial result (workspace) or final (o, lse)
+  int64_t dest0;                  // destination row of the piece's row 0
+  int64_t p0, L;
+  int n_pt;
+  PieceCursor nxt;
+  if (a.balanced) {
+    const PieceCursor cur = uniform_cursor(s_cur);
+    int64_t bs;
+    if (!band_cursor_piece(a, cur, bs)) break;
+    b = cur.b;
+    rb = cur.k * kBandRowBlocks + cur.slot;
+    const int64_t be = bs + cur.Tb;
+    t0 = (int)(max(cur.X0, bs) - bs);
+    t1 = (int)(min(cur.X1, be) - bs);
+    to_part = !(bs >= cur.X0 && be <= cur.X1);   // a piece of a band cut by a window edge
+    dest0 = to_part ? (int64_t)band_part_slot(cur.win, cur.slot, bs < cur.X0) * ROWS
+                    : (int64_t)b * n_rows + (int64_t)rb * ROWS;
+    nxt = cur;
+    band_cursor_next(a, nxt);
+    p0 = a.prefix_offsets[b];
+    L = max<int64_t>(a.prefix_offsets[b + 1] - p0, 0);
+    n_pt = (int)((L + KT - 1) / KT);
+    const int last_row = min(n_rows - 1, rb * ROWS + ROWS - 1);
+    t1 = min(t1, n_pt + (last_row / a.H) / KT + 1);   // tree tiles this row block can see
+  } else {
+    // uniform KV splits: one piece, item (request, row block, split)
+    if (single_done) break;
+    single_done = true;
+    int item = xcd_local_item(blockIdx.x, gridDim.x);
+    const int split = item % a.splits;
+    item /= a.splits;
+    rb = item % n_rb;
+    b = item / n_rb;
+    p0 = a.prefix_offsets[b];
+    L = max<int64_t>(a.prefix_offsets[b + 1] - p0, 0);
+    n_pt = (int)((L + KT - 1) / KT);
+    const int last_row = min(n_rows - 1, rb * ROWS + ROWS - 1);
+    const int n_tt = (last_row / a.H) / KT + 1;     // tree tiles that any row here can see
+    const int T = n_pt + n_tt;
+    t0 = (int)((int64_t)split * T / a.splits);
+    t1 = (int)((int64_t)(split + 1) * T / a.splits);
+    const int64_t row0 = (int64_t)b * n_rows + (int64_t)rb * ROWS;
+    to_part = a.splits > 1;
+    dest0 = to_part ? (int64_t)split * total_rows + row0 : row0;
+  }
 
   // ---- per-row mask words (LDS) ----
   const int W = (a.N + 31) >> 5;
@@ -327,30 +551,6 @@ verify_attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // ---- LDS addresses (lane constants) ----
-  const int kbase = lr * C_ROW + ((g ^ swz(lr)) << 4);   // K fragment, k-step 0
-  // V^T fragment (A of O^T) by transpose read.  Lane = 16 G + 4 rr + cc reads key
-  // 16 ks + 4 g + rr (+8 for the second read), dims 32 db + 16 (G & 1) + 4 cc .. +3,
-  // i.e. logical chunk 4 db + 2 (G & 1) + (cc >> 1), byte 8 (cc & 1) in it.
-  int voff;
-  {
-    const int G = lane >> 4;
-    const int rr = (lane >> 2) & 3;
-    const int cc = lane & 3;
-    const int vkey = 4 * g + rr;
-    voff = vkey * C_ROW + (((2 * (G & 1) + (cc >> 1)) ^ swz(vkey)) << 4) + (cc & 1) * 8;
-  }
-  const int voff_hi = (voff ^ 32) + 8 * C_ROW;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)s_kv;   // LDS byte address of the ring
-  CopyLanes clanes;
-  {
-    clanes.lw = (uint32_t)((lane << 4) ^ (wave << 6));
-    const int pr = wave * 4 + (lane >> 4);
-    const int logical = (lane & 15) ^ (pr & 7);
-    clanes.rkey = 2 * pr + (logical >> 3);
-    clanes.rpiece = (uint32_t)((logical & 7) * 16);
-  }
-
   // ---- accumulators and softmax state (one query row per lane) ----
   // Each row's probabilities are taken relative to a fixed reference m_ref:
   // the maximum score of the first tile in which the row sees any key (the
@@ -369,6 +569,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
   // Ring slot 2 starts zeroed: the first PV of a pass runs on it with a zero P.
   for (int i = tid; i < TILE_BYTES / 16; i += 256)
     reinterpret_cast<uint4*>(s_kv + 2 * TILE_BYTES)[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  if (a.balanced && tid == 0) s_cur = nxt;   // read again after the next piece's first barrier
 
   for (int pass = 0; pass < 2; ++pass) {
   bool overflow = false;
@@ -391,13 +593,29 @@ verify_attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < LOADS_PER_WAVE; ++i) issue_copy(cp0, clanes, lds0, wave, i);
   }
   int slot = 2;                          // ring slot of tile t (t0 - 1: none)
+  bool lo_t = false;                     // tile t carries a second P term (s_plo)
 
   for (int t = t0 - 1; t < t1; ++t) {
     const int slot_n = slot == 2 ? 0 : slot + 1;      // tile t + 1
     const int slot_d = slot_n == 2 ? 0 : slot_n + 1;  // tile t + 2
     const int tn = t + 1;
+
+    // ---- second term of P for tile t (slow-path tiles only): O^T += V^T . P_lo^T,
+    // P_lo staged by this lane in s_plo when tile t was prepared ----
+    if (lo_t) {
+      const unsigned char* buf = s_kv + slot * TILE_BYTES;
+      const bf16x8* pl = reinterpret_cast<const bf16x8*>(s_plo + (wave * 64 + lane) * 32);
+      const bf16x8 plo0 = pl[0], plo1 = pl[1];
+#pragma unroll
+      for (int st = 0; st < 2 * (DL / 32); ++st) {
+        const int ks = st / (DL / 32), db = st % (DL / 32);
+        mfma_o(oacc[db], load_vt(buf, voff, voff_hi, ks, db), ks ? plo1 : plo0);
+      }
+    }
+
     f32x16 sn;                    // S^T, then exponents, of tile tn
     float c, m, m_abs;
+    bool lo_n = false;            // tile tn carries a second P term
     if (tn < t1) {
       wait_copies();              // this wave's copies of tile tn have landed
       __syncthreads();            // ... and every wave's; every wave is done with tile t - 1
@@ -490,6 +708,30 @@ verify_attn_bf16_kernel(AttnArgs a) {
         c = 1.f;
         m = 0.f;
         m_abs = m_use;
+        // P = hi + lo with both terms bf16: hi is what the shadow below rounds
+        // 2^sn to (the same exp2 of the same exponent), lo the rounded
+        // remainder, applied by a second O^T pass over this tile next
+        // iteration.  Tiles on this path (tree tiles, a partial last prefix
+        // tile, a row's first visible tile) hold every key of the rows that see
+        // only a few, where a single bf16 term would leave a 2^-9 relative
+        // error uncancelled.
+        {
+          bf16x8 lo[2];
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(sn[e]), p1 = __builtin_amdgcn_exp2f(sn[e + 1]);
+            bf16x2 pr;
+            pr[0] = (__bf16)(p0 - (float)(__bf16)p0);
+            pr[1] = (__bf16)(p1 - (float)(__bf16)p1);
+            lo[e >> 3][e & 7] = pr[0];
+            lo[e >> 3][(e + 1) & 7] = pr[1];
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, kBf16Ones, l_run, false);
+          }
+          bf16x8* pl = reinterpret_cast<bf16x8*>(s_plo + (wave * 64 + lane) * 32);
+          pl[0] = lo[0];
+          pl[1] = lo[1];
+        }
+        lo_n = true;
       }
     } else {
       // nothing after this tile: the shadow work below evaluates to p = 0
@@ -523,7 +765,9 @@ verify_attn_bf16_kernel(AttnArgs a) {
           mfma_o(oacc[db], vf, pb[ks]);
         // three-stage pipeline over the 16 elements, so that the VALU work of one
         // step is independent: exponent of element st, 2^x and row max of st - 1,
-        // exp-sum and bf16 pair of st - 2
+        // bf16 pair and exp-sum of st - 2.  The exp-sum adds the bf16-rounded
+        // values the O^T MFMAs use (one dot2 per pair), so the weights applied
+        // to V sum to exactly the normaliser.
         if (st < 16) sn[st] = __builtin_fmaf(sn[st], c, -m);
         if (st >= 1 && st <= 16) {
           pe[st - 1] = __builtin_amdgcn_exp2f(sn[st - 1]);
@@ -531,10 +775,13 @@ verify_attn_bf16_kernel(AttnArgs a) {
         }
         if (st >= 2 && st <= 17) {
           const int e = st - 2;
-          l_run += pe[e];
           if (e & 1) {
-            pn[e >> 3][(e - 1) & 7] = (__bf16)pe[e - 1];
-            pn[e >> 3][e & 7] = (__bf16)pe[e];
+            bf16x2 pr;
+            pr[0] = (__bf16)pe[e - 1];
+            pr[1] = (__bf16)pe[e];
+            pn[e >> 3][(e - 1) & 7] = pr[0];
+            pn[e >> 3][e & 7] = pr[1];
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, kBf16Ones, l_run, false);
           }
         }
         if (st == 18) mx = halves_max(mx);
@@ -548,6 +795,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
     pb[0] = pn[0];
     pb[1] = pn[1];
     slot = slot_n;
+    lo_t = lo_n;
   }
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");   // last O^T MFMA -> AGPR reads / rewrites
   wait_copies();   // the repeated copy of the last tile (if any) has landed
@@ -559,19 +807,11 @@ verify_attn_bf16_kernel(AttnArgs a) {
 
   // ---- epilogue ----
   const float l_tot = halves_sum(l_run);
-  if (!row_ok) return;
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-  float* orow;
-  float* lrow;
-  if (a.splits == 1) {
-    orow = a.o + grow * DL;
-    lrow = a.lse + grow;
-  } else {
-    const int64_t total_rows = (int64_t)a.B * n_rows;
-    orow = a.part_o + ((int64_t)split * total_rows + grow) * DL;
-    lrow = a.part_lse + (int64_t)split * total_rows + grow;
-  }
+  if (row_ok) {
+  float* orow = (to_part ? a.part_o : a.o) + (dest0 + row_local) * DL;
+  float* lrow = (to_part ? a.part_lse : a.lse) + dest0 + row_local;
   // oacc[db][4 jj + i] is dim 32 db + 8 jj + 4 g + i of row lr
 #pragma unroll
   for (int db = 0; db < DL / 32; ++db) {
@@ -586,6 +826,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
     }
   }
   if (g == 0) *lrow = lse;
+  }
+  }   // pieces
 }
 
 // Merge split partials: lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.
@@ -613,9 +855,64 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
     acc.z += w * v.z;
     acc.w += w * v.w;
   }
-  const float inv = 1.f / wsum;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   reinterpret_cast<float4*>(o + row * Dl)[c4] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (c4 == 0) lse[row] = mx + logf(wsum);
+  if (c4 == 0) lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+}
+
+// Band schedule: merge the pieces of every band cut by a window edge.
+// Workgroup (edge e, slot j, group g) takes rows 8 g .. 8 g + 7 of row block j of
+// the band that edge e cuts first (described by the attention kernel), if any:
+// the tail piece of window e - 1 and the head pieces of the later windows the
+// band reaches.  32 threads per row, 4 float4 columns each.
+constexpr int kCombineRowsPerGroup = 8;
+constexpr int kCombineGroups = ROWS / kCombineRowsPerGroup;
+
+__global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
+  const int e = 1 + (int)blockIdx.x / (kBandRowBlocks * kCombineGroups);
+  const int j = ((int)blockIdx.x / kCombineGroups) % kBandRowBlocks;
+  const int grp = (int)blockIdx.x % kCombineGroups;
+  const int4 d = reinterpret_cast<const int4*>(a.band_edges)[e];
+  if (!d.x) return;
+  const int b = d.y, kb = d.z;
+  const unsigned heads = (unsigned)d.w;
+  const int n_rows = a.N * a.H;
+  const int rl = grp * kCombineRowsPerGroup + ((int)threadIdx.x >> 5);
+  const int r = (kb * kBandRowBlocks + j) * ROWS + rl;
+  if (r >= n_rows) return;
+  const int tail_slot = band_part_slot(e - 1, j, false);
+  float mx = a.part_lse[tail_slot * ROWS + rl];
+  for (int x = e; x < kBandWindows; ++x)
+    if (heads >> x & 1u) mx = fmaxf(mx, a.part_lse[band_part_slot(x, j, true) * ROWS + rl]);
+  float wsum = 0.f;
+  float4 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int c0 = threadIdx.x & 31;
+  for (int x = e - 1; x < kBandWindows; ++x) {
+    if (x >= e && !(heads >> x & 1u)) continue;
+    const int slot = x == e - 1 ? tail_slot : band_part_slot(x, j, true);
+    const float ls = a.part_lse[slot * ROWS + rl];
+    if (ls == -INFINITY) continue;
+    const float w = expf(ls - mx);
+    wsum += w;
+    const float4* src = reinterpret_cast<const float4*>(a.part_o + ((int64_t)slot * ROWS + rl) * DL);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 v = src[c0 + 32 * k];
+      acc[k].x += w * v.x;
+      acc[k].y += w * v.y;
+      acc[k].z += w * v.z;
+      acc[k].w += w * v.w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t grow = (int64_t)b * n_rows + r;
+  float4* dst = reinterpret_cast<float4*>(a.o + grow * DL);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    dst[c0 + 32 * k] = make_float4(acc[k].x * inv, acc[k].y * inv, acc[k].z * inv, acc[k].w * inv);
+  if (c0 == 0) a.lse[grow] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 }  // namespace
@@ -623,7 +920,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   const int n_rb = (a.N * a.H + ROWS - 1) / ROWS;
-  const int grid = a.B * n_rb * a.splits;
+  const int grid = a.balanced ? kBandWindows * kBandRowBlocks : a.B * n_rb * a.splits;
   hipLaunchKernelGGL(verify_attn_bf16_kernel, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -635,6 +932,13 @@ hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.part_o, a.part_lse,
                      a.splits, total_rows, a.Dl, a.o, a.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_band_combine(const AttnArgs& a, hipStream_t stream) {
+  if (a.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_band_combine_kernel, dim3((kBandWindows - 1) * kBandRowBlocks * kCombineGroups), dim3(256),
+                     0, stream, a);
   return hipGetLastError();
 }
 

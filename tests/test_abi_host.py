@@ -123,17 +123,33 @@ def test_workspace_contract():
     assert attn(splits=-1) == INVALID
 
 
-def test_auto_split_heuristic():
+# (window, slot, head/tail) partial slots of 128 rows x (Dl + 1) floats, then 8 edge descriptors of 4 ints
+BAND_WS = 2 * 8 * 32 * 128 * 513 * 4 + 8 * 16
+
+
+def test_auto_schedule():
     lib = dd.lib()
-    # one request of 64 nodes x 64 heads = 32 row blocks: 8 splits cover 256 CUs
-    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 64, 64, 512, 64, 4096) == 8
-    # 4 x 128 nodes x 64 heads = 256 row blocks: no split
-    assert lib.ddtree_verify_attn_auto_splits(BF16, 4, 128, 64, 512, 64, 131072) == 1
-    # short prefixes are not split below 4 tiles per split
-    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 32) == 1
+    # row blocks (128 rows each) in whole bands of 32: the band schedule (0)
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 64, 64, 512, 64, 4096) == 0       # 32 row blocks
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 4, 128, 64, 512, 64, 131072) == 0    # 64 per request
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 16, 64, 64, 512, 64, 32768) == 0
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 3, 32, 128, 512, 64, 10) == 0
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 0) == BAND_WS
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 16, 64, 64, 512, 64, 32768, 0) == BAND_WS
+    # otherwise uniform splits: enough workgroups to cover 256 CUs, at least 4 tiles per split
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 4096) == 32       # 4 row blocks, 129 tiles / 4
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 40, 64, 512, 64, 4096) == 13      # 20 row blocks
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 40, 64, 512, 64, 4096, 0) == 13 * 40 * 64 * 513 * 4
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 32) == 1          # 2 tiles: no split
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 9, 40, 64, 512, 64, 4096) == 2       # 180 row blocks
     assert lib.ddtree_verify_attn_auto_splits(F32, 1, 8, 4, 64, 32, 4096) == 1
-    ws = lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 0)
-    assert ws == 8 * 64 * 64 * 513 * 4
+    assert lib.ddtree_verify_attn_workspace_size(F32, 1, 64, 64, 64, 32, 4096, 0) == 0
+    # an explicit split count always takes the uniform schedule
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 1) == 0
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 8) == 8 * 64 * 64 * 513 * 4
+    # the band schedule needs its workspace like any split
+    assert attn(N=64, splits=0) == WORKSPACE
+    assert attn(N=64, splits=0, ws=A + (8 << 24), ws_bytes=BAND_WS - 4) == WORKSPACE
 
 
 # ---------------------------------------------------------------- greedy_accept

@@ -212,6 +212,41 @@ def test_attn_bf16_split_invariance_and_determinism():
         compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
 
 
+@pytest.mark.parametrize("case", [
+    # ragged prefixes (empty, sub-tile, tile edges, thousands): several bands cut by window edges
+    dict(B=12, N=64, H=64, prefix=("list", [0, 1, 31, 32, 33, 1500, 700, 2900, 64, 5, 3100, 950]),
+         tree=("bounded", 8, 4)),
+    # one request with an empty prefix: 2 tile columns over 8 windows, six of them empty
+    dict(B=1, N=64, H=64, prefix=("fixed", 0), tree=("bounded", 8, 4)),
+    # one long request: its band is cut into 8 pieces
+    dict(B=1, N=64, H=64, prefix=("fixed", 5000), tree=("uniform",)),
+    # two bands per request (128 nodes x 64 heads = 64 row blocks)
+    dict(B=3, N=128, H=64, prefix=("list", [2500, 40, 900]), tree=("bounded", 12, 4)),
+    # more requests than one 64-lane scan chunk (32 nodes x 128 heads)
+    dict(B=66, N=32, H=128, prefix=("uniform", 0, 96), tree=("uniform",)),
+])
+def test_attn_bf16_band_schedule(case):
+    """The automatic band schedule (row blocks in groups of 32, KV columns cut into 8 equal
+    windows): every output row, whole or merged from pieces, matches the oracle, and a
+    repeated call is bitwise identical."""
+    params = dict(K2)
+    params.update(case)
+    w = make_workload(seed=31, **params)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, dw.max_len) == 0
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    o2, lse2 = dw.attn(mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    nodes = None
+    if w.B > 32:
+        nodes = [(b, i) for b in (0, 31, 63, 64, w.B - 1) for i in (0, w.N // 2, w.N - 1)]
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    print(f"band schedule B={w.B} N={w.N} H={w.H}: normwise o err {eo:.2e}, lse err {el:.2e}")
+
+
 def _bf16_bits(x):
     from synth import bf16_bits
     return bf16_bits(np.asarray(x, np.float32))
