@@ -10,10 +10,13 @@
 // Native DDTree Speculative Decoding Engine", section "The Output Knowledge
 // Created").
 //
-// accept_argmax: one 1024-thread workgroup per logits row streams the row
-// with 16-byte loads (8 in flight per thread) and keeps (max, first index)
-// per thread; waves reduce with shuffles, the block through LDS.  Ties go to
-// the lowest index, so the result does not depend on the reduction order.
+// accept_argmax: one 512-thread workgroup per logits row streams the row
+// with 16-byte nontemporal loads (10 in flight per thread) and keeps (max,
+// first index) per thread: a thread visits its elements in increasing index
+// order, so a strict comparison keeps the first of equal values with one
+// compare per element.  Waves reduce with shuffles, the block through LDS,
+// both with an explicit lowest-index tie rule, so the result does not depend
+// on the reduction order.  NaN never compares greater and is never chosen.
 // accept_path: one workgroup per request, one thread per node; each thread
 // walks its ancestor chain (bounded by N) to decide whether its root path
 // matches, the deepest matching node (smallest index on ties) is found with
@@ -28,8 +31,8 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kArgmaxThreads = 1024;
-constexpr int kUnroll = 8;
+constexpr int kArgmaxThreads = 512;
+constexpr int kUnroll = 10;
 
 struct ValIdx {
   float v;
@@ -44,16 +47,26 @@ __device__ __forceinline__ void take_if_better(ValIdx& best, float v, int i) {
   }
 }
 
+// a thread's own scan: indices only grow, so equal values keep the earlier one
+__device__ __forceinline__ void take_if_greater(ValIdx& best, float v, int i) {
+  if (v > best.v) {
+    best.v = v;
+    best.i = i;
+  }
+}
+
 template <bool kVec>
 __global__ void __launch_bounds__(kArgmaxThreads) argmax_kernel(const float* __restrict__ logits, int64_t ld, int V,
                                                                 int32_t* __restrict__ out) {
   const int64_t row = blockIdx.x;
   const float* p = logits + row * ld;
   const int tid = threadIdx.x;
+  // start from (-inf, the thread's first index), so a row of -inf gives its first index
   ValIdx best{-__builtin_inff(), INT_MAX};
 
   if (kVec) {
     const int nvec = V >> 2;
+    best.i = tid < nvec ? tid << 2 : ((nvec << 2) + tid < V ? (nvec << 2) + tid : INT_MAX);
     const f32x4* p4 = reinterpret_cast<const f32x4*>(p);
     int c = tid;
     // main loop: kUnroll independent 16-byte loads in flight per thread
@@ -64,23 +77,24 @@ __global__ void __launch_bounds__(kArgmaxThreads) argmax_kernel(const float* __r
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int base = (c + u * kArgmaxThreads) << 2;
-        take_if_better(best, x[u].x, base);
-        take_if_better(best, x[u].y, base + 1);
-        take_if_better(best, x[u].z, base + 2);
-        take_if_better(best, x[u].w, base + 3);
+        take_if_greater(best, x[u].x, base);
+        take_if_greater(best, x[u].y, base + 1);
+        take_if_greater(best, x[u].z, base + 2);
+        take_if_greater(best, x[u].w, base + 3);
       }
     }
     for (; c < nvec; c += kArgmaxThreads) {
       const f32x4 x = p4[c];
       const int base = c << 2;
-      take_if_better(best, x.x, base);
-      take_if_better(best, x.y, base + 1);
-      take_if_better(best, x.z, base + 2);
-      take_if_better(best, x.w, base + 3);
+      take_if_greater(best, x.x, base);
+      take_if_greater(best, x.y, base + 1);
+      take_if_greater(best, x.z, base + 2);
+      take_if_greater(best, x.w, base + 3);
     }
-    for (int e = (nvec << 2) + tid; e < V; e += kArgmaxThreads) take_if_better(best, p[e], e);
+    for (int e = (nvec << 2) + tid; e < V; e += kArgmaxThreads) take_if_greater(best, p[e], e);
   } else {
-    for (int e = tid; e < V; e += kArgmaxThreads) take_if_better(best, p[e], e);
+    best.i = tid < V ? tid : INT_MAX;
+    for (int e = tid; e < V; e += kArgmaxThreads) take_if_greater(best, p[e], e);
   }
 
   // wave reduction
