@@ -39,10 +39,16 @@
 //  * MFMAs are issued by inline asm to pin S^T to VGPRs and O^T to AGPRs;
 //    LDS fragment reads run 4 MFMAs ahead; workgroups are mapped so that a
 //    request's row blocks share one XCD's L2.
+//  * On tiles of the slow path (tree tiles, a partial last prefix tile, a
+//    row's first visible tile) P is applied as two bf16 terms, hi + lo, so
+//    rows that see only a few keys keep about 16 bits of each weight; the
+//    exp-sum adds exactly the bf16 values applied.
 //  * Prefix tiles first, then tree tiles; the ancestor mask is one 32-bit
-//    word per row per tree tile.  Long prefixes can be split across
-//    workgroups (flash-decoding); partials are merged by the combine kernel
-//    with the log-sum-exp weights.
+//    word per row per tree tile.
+//  * Scheduling: the band schedule (below) balances ragged batches over the
+//    CUs and keeps each XCD on one KV stream; otherwise long prefixes can be
+//    split uniformly across workgroups (flash-decoding).  Partials are merged
+//    by a combine kernel with the log-sum-exp weights.
 #include <cmath>
 
 #include "ddtree_internal.h"
