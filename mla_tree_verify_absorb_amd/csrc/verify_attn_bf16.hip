@@ -177,14 +177,58 @@ __device__ __forceinline__ CopyPlan copy_plan(const AttnArgs& a, int b, int64_t 
   return q;
 }
 
-__device__ __forceinline__ void issue_copy(const CopyPlan& q, const CopyLanes& cl, uint32_t lds_buf, int wave, int i) {
-  if (i < C_LOADS_PER_WAVE) {
-    const int key = wave + NWAVES * i;
+// The lane's address is formed inside the asm statement, between the M0 write
+// and the load: that covers the one wait state an LDS DMA needs after M0 is
+// written, and the compiler cannot precompute per-copy lane values (which it
+// would keep in VGPRs across the tile loop).
+// Latent copy: lane address (lw ^ xr) + rowoff, with xr = 16 (i & 3) an inline constant.
+template <int XR>
+__device__ __forceinline__ void lds_dma16_latent(uint32_t lds_base, const void* gbase, uint32_t lw, uint32_t rowoff) {
+  uint32_t addr;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "v_xad_u32 %0, %2, %3, %4\n\t"
+      "global_load_lds_dwordx4 %0, %5"
+      : "=&v"(addr)
+      : "s"(lds_base), "v"(lw), "i"(XR), "s"(rowoff), "s"(gbase)
+      : "memory");
+}
+// Rotary copy: lane address rowoff + piece.
+__device__ __forceinline__ void lds_dma16_rotary(uint32_t lds_base, const void* gbase, uint32_t rowoff, uint32_t piece) {
+  uint32_t addr;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "v_add_u32_e32 %0, %2, %3\n\t"
+      "global_load_lds_dwordx4 %0, %4"
+      : "=&v"(addr)
+      : "s"(lds_base), "v"(rowoff), "v"(piece), "s"(gbase)
+      : "memory");
+}
+
+template <int I>
+__device__ __forceinline__ void issue_copy(const CopyPlan& q, const CopyLanes& cl, uint32_t lds_buf, int wave) {
+  if constexpr (I < C_LOADS_PER_WAVE) {
+    const int key = wave + NWAVES * I;
     const uint32_t kc = (uint32_t)min(key, q.count - 1);
-    lds_dma16(lds_buf + key * C_ROW, q.c, (opaque(cl.lw) ^ (uint32_t)((i & 3) << 4)) + kc * q.cstride);
+    lds_dma16_latent<(I & 3) << 4>(lds_buf + key * C_ROW, q.c, cl.lw, kc * q.cstride);
   } else {
     const uint32_t kc = (uint32_t)min(opaque(cl.rkey), q.count - 1);
-    lds_dma16(lds_buf + R_OFF + wave * 1024, q.r, kc * q.rstride + opaque(cl.rpiece));
+    lds_dma16_rotary(lds_buf + R_OFF + wave * 1024, q.r, kc * q.rstride, cl.rpiece);
+  }
+}
+
+// Copy i of a tile, i a compile-time constant after unrolling.
+__device__ __forceinline__ void issue_copy(const CopyPlan& q, const CopyLanes& cl, uint32_t lds_buf, int wave, int i) {
+  switch (i) {
+    case 0: issue_copy<0>(q, cl, lds_buf, wave); break;
+    case 1: issue_copy<1>(q, cl, lds_buf, wave); break;
+    case 2: issue_copy<2>(q, cl, lds_buf, wave); break;
+    case 3: issue_copy<3>(q, cl, lds_buf, wave); break;
+    case 4: issue_copy<4>(q, cl, lds_buf, wave); break;
+    case 5: issue_copy<5>(q, cl, lds_buf, wave); break;
+    case 6: issue_copy<6>(q, cl, lds_buf, wave); break;
+    case 7: issue_copy<7>(q, cl, lds_buf, wave); break;
+    default: issue_copy<8>(q, cl, lds_buf, wave); break;
   }
 }
 

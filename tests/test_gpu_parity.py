@@ -247,6 +247,29 @@ def test_attn_bf16_band_schedule(case):
     print(f"band schedule B={w.B} N={w.N} H={w.H}: normwise o err {eo:.2e}, lse err {el:.2e}")
 
 
+@pytest.mark.parametrize("seed", [101, 102, 103])
+def test_attn_bf16_band_schedule_random_shapes(seed):
+    """Seeded random band-schedule shapes: request count, (nodes, heads) with whole bands of 32
+    row blocks, and a length mix of empty, sub-tile and long prefixes; sampled nodes of every
+    fifth request against the oracle."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 24))
+    N, H = [(64, 64), (32, 128), (128, 64)][int(rng.integers(0, 3))]
+    lens = [int(rng.choice([0, int(rng.integers(1, 40)), int(rng.integers(40, 6000))])) for _ in range(B)]
+    params = dict(K2)
+    params.update(B=B, N=N, H=H, prefix=("list", lens), tree=("bounded", 10, 4))
+    w = make_workload(seed=seed, **params)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, dw.max_len) == 0
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    torch.cuda.synchronize()
+    nodes = [(b, i) for b in range(0, B, 5) for i in sorted({0, N // 3, N - 1})]
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    print(f"seed {seed}: B={B} N={N} H={H} lens={lens}: normwise o err {eo:.2e}, lse err {el:.2e}")
+
+
 def _bf16_bits(x):
     from synth import bf16_bits
     return bf16_bits(np.asarray(x, np.float32))
