@@ -704,6 +704,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
                                                                (pair_chunk(row_local, cc) << 4));
           }
           if (s % 3 == 1 && s / 3 < LOADS_PER_WAVE) issue_copy(cplan, clanes, lds_d, wave, s / 3);
+          // one LDS wait per pair of MFMAs: K fragments s and s + 1 (3 younger reads in flight)
+          if (s % 2 == 0 && s + 1 < DL / 16 + DR / 16) __builtin_amdgcn_s_waitcnt(0xC37F);
           if (s == 0)
             mfma_s_first(sn, kf, qv);
           else if (s == DL / 16 + DR / 16 - 1)
@@ -809,6 +811,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
         const int ks = st / (DL / 32), db = st % (DL / 32);
         const bf16x8 vf = vring[st % VRING];
         if (st + VRING < NST) vring[st % VRING] = load_vt(buf, voff, voff_hi, (st + VRING) / (DL / 32), (st + VRING) % (DL / 32));
+        // one LDS wait per pair of MFMAs: V^T fragments st and st + 1 (3 younger pairs in flight)
+        if (st % 2 == 0 && st + 4 < NST) __builtin_amdgcn_s_waitcnt(0xC67F);
         if (st == 0)
           mfma_o_first(oacc[db], vf, pb[ks]);
         else
