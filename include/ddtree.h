@@ -99,8 +99,9 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *                                              the value up-projection)
  *     lse[b,i,h] = ln sum_j exp(s_j)
  *
- *   dtype            DDTREE_BF16: (Dl, Dr) = (512, 64) on the MFMA kernel;
- *                    DDTREE_F32: any Dl in 1..512, Dr in 0..512
+ *   dtype            DDTREE_BF16 at (Dl, Dr) = (512, 64): the MFMA kernel;
+ *                    DDTREE_F32, and DDTREE_BF16 at other dims: the generic
+ *                    kernel (float32 arithmetic), any Dl in 1..512, Dr in 0..512
  *   B, N, H          requests, nodes per request (<= DDTREE_MAX_NODES), heads
  *   q_lat            device [B, N, H, Dl], dense
  *   q_rope           device [B, N, H, Dr], dense
@@ -123,7 +124,8 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *                    groups' KV tiles laid end to end and cut into 8 equal
  *                    ranges, one per XCD (32 workgroups each), so that every CU
  *                    carries the same work however ragged the prefix lengths;
- *                    otherwise uniform splits (ddtree_verify_attn_auto_splits)
+ *                    otherwise uniform splits (ddtree_verify_attn_auto_splits).
+ *                    MFMA kernel only; the generic kernel ignores it.
  *   o                device float32 [B, N, H, Dl]
  *   lse              device float32 [B, N, H] (natural log)
  *   workspace        device scratch of workspace_bytes >=
@@ -132,9 +134,10 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *                    splits take S*B*N*H*(Dl+1) floats, the band schedule
  *                    512*128*(Dl+1) floats plus 128 bytes (134.5 MB)
  *                    whatever B
- * bf16 inputs need 16-byte aligned base pointers and row strides that are
- * multiples of 8 elements (INVALID_ARG otherwise) and at most 2^24 elements
- * (UNSUPPORTED otherwise).  Requests whose tree_ok is 0 give undefined o/lse.
+ * bf16 inputs on the MFMA kernel need 16-byte aligned base pointers and row
+ * strides that are multiples of 8 elements (INVALID_ARG otherwise) and at most
+ * 2^24 elements (UNSUPPORTED otherwise); on the generic kernel, 2-byte aligned
+ * pointers.  Requests whose tree_ok is 0 give undefined o/lse.
  */
 size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                          int64_t max_prefix_len, int32_t num_splits);

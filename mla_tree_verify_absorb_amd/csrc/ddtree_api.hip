@@ -50,12 +50,14 @@ int copy_unit(const void* a, int64_t lda_bytes, const void* b, int64_t ldb_bytes
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool bf16_shape_supported(int Dl, int Dr) { return Dl == kMfmaDl && Dr == kMfmaDr; }
+// bf16 at (Dl, Dr) = (512, 64) runs on the MFMA kernel; every other supported
+// case (fp32, bf16 at other dims) on the generic kernel, which never splits.
+bool mfma_path(int dtype, int Dl, int Dr) { return dtype == DDTREE_BF16 && Dl == kMfmaDl && Dr == kMfmaDr; }
 
 // KV splits per query block: enough workgroups to cover the 256 CUs once,
 // while every split keeps at least 4 KV tiles (128 keys).
-int auto_splits(int dtype, int B, int N, int H, int64_t max_prefix_len) {
-  if (dtype != DDTREE_BF16 || B <= 0 || N <= 0 || H <= 0) return 1;
+int auto_splits(bool mfma, int B, int N, int H, int64_t max_prefix_len) {
+  if (!mfma || B <= 0 || N <= 0 || H <= 0) return 1;
   const int64_t n_rb = ceil_div((int64_t)N * H, kRowsPerBlock);
   const int64_t wg = (int64_t)B * n_rb;
   int64_t s = wg >= 256 ? 1 : ceil_div(256, wg);
@@ -68,23 +70,23 @@ int auto_splits(int dtype, int B, int N, int H, int64_t max_prefix_len) {
 
 // The automatic schedule is the band schedule whenever a request's row blocks
 // come in whole bands of kBandRowBlocks; 0 stands for it.
-bool band_schedule_applies(int dtype, int N, int H) {
-  return dtype == DDTREE_BF16 && ceil_div((int64_t)N * H, kRowsPerBlock) % kBandRowBlocks == 0;
+bool band_schedule_applies(bool mfma, int N, int H) {
+  return mfma && ceil_div((int64_t)N * H, kRowsPerBlock) % kBandRowBlocks == 0;
 }
 
-int auto_schedule(int dtype, int B, int N, int H, int64_t max_prefix_len) {
-  if (band_schedule_applies(dtype, N, H)) return 0;
-  return auto_splits(dtype, B, N, H, max_prefix_len);
+int auto_schedule(bool mfma, int B, int N, int H, int64_t max_prefix_len) {
+  if (band_schedule_applies(mfma, N, H)) return 0;
+  return auto_splits(mfma, B, N, H, max_prefix_len);
 }
 
 // Uniform split count (>= 1), or 0 for the band schedule.
-int resolve_splits(int dtype, int B, int N, int H, int64_t max_prefix_len, int num_splits) {
-  if (dtype != DDTREE_BF16) return 1;
-  return num_splits > 0 ? num_splits : auto_schedule(dtype, B, N, H, max_prefix_len);
+int resolve_splits(bool mfma, int B, int N, int H, int64_t max_prefix_len, int num_splits) {
+  if (!mfma) return 1;
+  return num_splits > 0 ? num_splits : auto_schedule(mfma, B, N, H, max_prefix_len);
 }
 
-size_t workspace_bytes_for(int dtype, int B, int N, int H, int Dl, int splits) {
-  if (dtype != DDTREE_BF16) return 0;
+size_t workspace_bytes_for(bool mfma, int B, int N, int H, int Dl, int splits) {
+  if (!mfma) return 0;
   if (splits == 0)
     return (size_t)kBandPartSlots * kRowsPerBlock * (uint64_t)(Dl + 1) * sizeof(float) + kBandWindows * 4 * sizeof(int);
   if (splits == 1) return 0;
@@ -126,18 +128,16 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
 
 int32_t ddtree_verify_attn_auto_splits(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                        int64_t max_prefix_len) {
-  (void)Dl;
-  (void)Dr;
   if (B <= 0 || N <= 0 || H <= 0) return 1;
-  return auto_schedule(dtype, B, N, H, max_prefix_len);
+  return auto_schedule(mfma_path(dtype, Dl, Dr), B, N, H, max_prefix_len);
 }
 
 size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                          int64_t max_prefix_len, int32_t num_splits) {
-  (void)Dr;
   if (B <= 0 || N <= 0 || H <= 0 || Dl <= 0 || num_splits < 0) return 0;
-  const int s = resolve_splits(dtype, B, N, H, max_prefix_len, num_splits);
-  return workspace_bytes_for(dtype, B, N, H, Dl, s);
+  const bool mfma = mfma_path(dtype, Dl, Dr);
+  const int s = resolve_splits(mfma, B, N, H, max_prefix_len, num_splits);
+  return workspace_bytes_for(mfma, B, N, H, Dl, s);
 }
 
 int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr, const void* q_lat,
@@ -151,8 +151,8 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   if (B < 0 || N < 1 || H < 1 || Dl < 1 || Dr < 0 || num_splits < 0 || max_prefix_len < 0)
     return DDTREE_ERR_INVALID_ARG;
   if (N > DDTREE_MAX_NODES) return DDTREE_ERR_UNSUPPORTED;
-  if (dtype == DDTREE_BF16 && !bf16_shape_supported(Dl, Dr)) return DDTREE_ERR_UNSUPPORTED;
-  if (dtype == DDTREE_F32 && (Dl > 512 || Dr > 512)) return DDTREE_ERR_UNSUPPORTED;
+  const bool mfma = mfma_path(dtype, Dl, Dr);
+  if (!mfma && (Dl > 512 || Dr > 512)) return DDTREE_ERR_UNSUPPORTED;
   if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
     return DDTREE_ERR_INVALID_ARG;
   if ((int64_t)B * N * H > INT32_MAX / 4) return DDTREE_ERR_UNSUPPORTED;
@@ -162,7 +162,14 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   if (Dr > 0 && (!q_rope || !krope_tree)) return DDTREE_ERR_INVALID_ARG;
   if (max_prefix_len > 0 && (!ckv || (Dr > 0 && !krope))) return DDTREE_ERR_INVALID_ARG;
   if (ld_ckv < Dl || ld_ckv_tree < Dl || ld_krope < Dr || ld_krope_tree < Dr) return DDTREE_ERR_INVALID_ARG;
-  if (dtype == DDTREE_BF16) {
+  if (dtype == DDTREE_BF16 && !mfma) {
+    // generic kernel: element loads only
+    const uintptr_t any = reinterpret_cast<uintptr_t>(q_lat) | reinterpret_cast<uintptr_t>(q_rope) |
+                          reinterpret_cast<uintptr_t>(ckv) | reinterpret_cast<uintptr_t>(krope) |
+                          reinterpret_cast<uintptr_t>(ckv_tree) | reinterpret_cast<uintptr_t>(krope_tree);
+    if (any & 1u) return DDTREE_ERR_INVALID_ARG;
+  }
+  if (mfma) {
     if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(ckv) || !aligned16(krope) || !aligned16(ckv_tree) ||
         !aligned16(krope_tree) || !aligned16(o))
       return DDTREE_ERR_INVALID_ARG;
@@ -173,9 +180,9 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
       return DDTREE_ERR_UNSUPPORTED;
   }
   // ---- workspace ----
-  const int splits = resolve_splits(dtype, B, N, H, max_prefix_len, num_splits);
+  const int splits = resolve_splits(mfma, B, N, H, max_prefix_len, num_splits);
   if (splits > 1024) return DDTREE_ERR_UNSUPPORTED;
-  const size_t need = workspace_bytes_for(dtype, B, N, H, Dl, splits);
+  const size_t need = workspace_bytes_for(mfma, B, N, H, Dl, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DDTREE_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return DDTREE_ERR_INVALID_ARG;
   // ---- aliasing (extents known on the host) ----
@@ -228,12 +235,12 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (dtype == DDTREE_BF16) {
+  if (mfma) {
     e = launch_verify_attn_bf16(a, s);
     if (e == hipSuccess && splits > 1) e = launch_attn_combine(a, s);
     if (e == hipSuccess && splits == 0) e = launch_attn_band_combine(a, s);
   } else {
-    e = launch_verify_attn_f32(a, s);
+    e = launch_verify_attn_generic(a, dtype == DDTREE_BF16, s);
   }
   return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
 }

@@ -74,7 +74,8 @@ struct CompactArgs {
 };
 
 hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_verify_attn_f32(const AttnArgs& a, hipStream_t stream);
+// fp32 arithmetic for fp32 or bf16 inputs, any Dl <= 512, Dr <= 512
+hipError_t launch_verify_attn_generic(const AttnArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_compact_kv(const CompactArgs& a, hipStream_t stream);
 // NeoX rotary embedding at tree positions
 constexpr int kMaxRopeDim = 512;

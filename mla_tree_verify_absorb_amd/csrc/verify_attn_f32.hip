@@ -1,4 +1,5 @@
-// Tree-verify attention, absorbed MLA form, float32 inputs and arithmetic.
+// Tree-verify attention, absorbed MLA form, float32 arithmetic on float32 or
+// bf16 inputs (bf16 widened exactly on load).
 //
 // What is computed (page "The Moment of Proof: Validating a Native CUDA
 // Speculative Decoding Engine", section "Input Knowledge Required": MLA in
@@ -9,8 +10,9 @@
 // natural log-sum-exp.
 //
 // This kernel serves the float32 workloads (the pages' tiny FP32 model has
-// kv_lora 64 with 4 heads): small, launch-latency-bound shapes where MFMA
-// tiles would sit mostly empty.  One workgroup per (request, node); each
+// kv_lora 64 with 4 heads) and bf16 inputs at dims other than the MFMA
+// kernel's (512, 64): small, launch-latency-bound shapes where MFMA tiles
+// would sit mostly empty.  One workgroup per (request, node); each
 // wave takes one head at a time.  Keys are visited in chunks of 64, one key
 // per lane for the score (q staged in LDS), then the chunk's probabilities
 // are broadcast and every lane accumulates its own output dimensions from
@@ -38,7 +40,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__global__ void __launch_bounds__(kWaves * 64) verify_attn_f32_kernel(AttnArgs a) {
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t bits) { return __builtin_bit_cast(float, (uint32_t)bits << 16); }
+
+template <typename T>
+__global__ void __launch_bounds__(kWaves * 64) verify_attn_generic_kernel(AttnArgs a) {
   __shared__ float s_q[kWaves][kMaxDq];
   const int bi = blockIdx.x;            // b * N + i
   const int b = bi / a.N;
@@ -47,12 +53,12 @@ __global__ void __launch_bounds__(kWaves * 64) verify_attn_f32_kernel(AttnArgs a
   const int Dl = a.Dl, Dr = a.Dr;
   const int W = (a.N + 31) >> 5;
 
-  const float* q_lat = static_cast<const float*>(a.q_lat);
-  const float* q_rope = static_cast<const float*>(a.q_rope);
-  const float* ckv = static_cast<const float*>(a.ckv);
-  const float* krope = static_cast<const float*>(a.krope);
-  const float* ckv_t = static_cast<const float*>(a.ckv_tree);
-  const float* krope_t = static_cast<const float*>(a.krope_tree);
+  const T* q_lat = static_cast<const T*>(a.q_lat);
+  const T* q_rope = static_cast<const T*>(a.q_rope);
+  const T* ckv = static_cast<const T*>(a.ckv);
+  const T* krope = static_cast<const T*>(a.krope);
+  const T* ckv_t = static_cast<const T*>(a.ckv_tree);
+  const T* krope_t = static_cast<const T*>(a.krope_tree);
   const uint32_t* mrow = a.mask + (int64_t)bi * W;
 
   const int64_t p0 = a.prefix_offsets[b];
@@ -62,8 +68,8 @@ __global__ void __launch_bounds__(kWaves * 64) verify_attn_f32_kernel(AttnArgs a
 
   for (int h = wave; h < a.H; h += kWaves) {
     const int64_t row = (int64_t)bi * a.H + h;
-    for (int d = lane; d < Dl; d += 64) s_q[wave][d] = q_lat[row * Dl + d];
-    for (int d = lane; d < Dr; d += 64) s_q[wave][Dl + d] = q_rope[row * Dr + d];
+    for (int d = lane; d < Dl; d += 64) s_q[wave][d] = widen(q_lat[row * Dl + d]);
+    for (int d = lane; d < Dr; d += 64) s_q[wave][Dl + d] = widen(q_rope[row * Dr + d]);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -77,8 +83,8 @@ __global__ void __launch_bounds__(kWaves * 64) verify_attn_f32_kernel(AttnArgs a
       const int64_t kk = k0 + lane;
       float s = -INFINITY;
       if (kk < total) {
-        const float* crow;
-        const float* rrow;
+        const T* crow;
+        const T* rrow;
         bool vis = true;
         if (kk < L) {
           crow = ckv + (p0 + kk) * a.ld_ckv;
@@ -91,8 +97,8 @@ __global__ void __launch_bounds__(kWaves * 64) verify_attn_f32_kernel(AttnArgs a
         }
         if (vis) {
           float dot = 0.f;
-          for (int d = 0; d < Dl; ++d) dot = fmaf(s_q[wave][d], crow[d], dot);
-          for (int d = 0; d < Dr; ++d) dot = fmaf(s_q[wave][Dl + d], rrow[d], dot);
+          for (int d = 0; d < Dl; ++d) dot = fmaf(s_q[wave][d], widen(crow[d]), dot);
+          for (int d = 0; d < Dr; ++d) dot = fmaf(s_q[wave][Dl + d], widen(rrow[d]), dot);
           s = dot * a.scale;
         }
       }
@@ -112,12 +118,12 @@ __global__ void __launch_bounds__(kWaves * 64) verify_attn_f32_kernel(AttnArgs a
         const float pj = __shfl(p, j, 64);
         if (pj == 0.f) continue;                   // wave-uniform
         const int64_t kj = k0 + j;
-        const float* crow = (kj < L) ? ckv + (p0 + kj) * a.ld_ckv
-                                     : ckv_t + ((int64_t)b * a.N + (kj - L)) * a.ld_ckv_tree;
+        const T* crow = (kj < L) ? ckv + (p0 + kj) * a.ld_ckv
+                                 : ckv_t + ((int64_t)b * a.N + (kj - L)) * a.ld_ckv_tree;
 #pragma unroll
         for (int t = 0; t < kMaxT; ++t) {
           const int d = lane + 64 * t;
-          if (d < Dl) acc[t] = fmaf(pj, crow[d], acc[t]);
+          if (d < Dl) acc[t] = fmaf(pj, widen(crow[d]), acc[t]);
         }
       }
     }
@@ -134,9 +140,12 @@ __global__ void __launch_bounds__(kWaves * 64) verify_attn_f32_kernel(AttnArgs a
 
 }  // namespace
 
-hipError_t launch_verify_attn_f32(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_verify_attn_generic(const AttnArgs& a, bool bf16, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(verify_attn_f32_kernel, dim3(a.B * a.N), dim3(kWaves * 64), 0, stream, a);
+  if (bf16)
+    hipLaunchKernelGGL(verify_attn_generic_kernel<uint16_t>, dim3(a.B * a.N), dim3(kWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(verify_attn_generic_kernel<float>, dim3(a.B * a.N), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

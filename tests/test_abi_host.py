@@ -80,8 +80,11 @@ def attn(dtype=BF16, B=1, N=8, H=64, Dl=512, Dr=64, q=A, qr=A + (1 << 24), ckv=A
 
 def test_verify_attn_shape_support():
     assert attn(dtype=7) == UNSUPPORTED
-    assert attn(Dl=256) == UNSUPPORTED                 # bf16 kernel is (512, 64)
-    assert attn(Dr=32) == UNSUPPORTED
+    # bf16 at (512, 64) runs on the MFMA kernel, other dims on the generic kernel up to 512 each
+    assert attn(Dl=1024, ld_ckv=1088, ld_ckv_t=1088) == UNSUPPORTED
+    assert attn(Dr=520, ld_krope=1040, ld_krope_t=1040) == UNSUPPORTED
+    assert attn(Dl=256, Dr=32, q=A + 1) == INVALID     # generic bf16 path: 2-byte alignment
+    assert attn(Dl=256, Dr=32, ckv=A + (2 << 24) + 1) == INVALID
     assert attn(dtype=F32, Dl=1024) == UNSUPPORTED
     assert attn(N=257) == UNSUPPORTED
     assert attn(N=0) == INVALID
@@ -143,6 +146,10 @@ def test_auto_schedule():
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 32) == 1          # 2 tiles: no split
     assert lib.ddtree_verify_attn_auto_splits(BF16, 9, 40, 64, 512, 64, 4096) == 2       # 180 row blocks
     assert lib.ddtree_verify_attn_auto_splits(F32, 1, 8, 4, 64, 32, 4096) == 1
+    # bf16 away from the MFMA dims takes the generic kernel: no split, no workspace
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 64, 64, 256, 32, 4096) == 1
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 256, 32, 4096, 0) == 0
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 256, 32, 4096, 8) == 0
     assert lib.ddtree_verify_attn_workspace_size(F32, 1, 64, 64, 64, 32, 4096, 0) == 0
     # an explicit split count always takes the uniform schedule
     assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 1) == 0

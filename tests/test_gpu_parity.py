@@ -270,6 +270,27 @@ def test_attn_bf16_band_schedule_random_shapes(seed):
     print(f"seed {seed}: B={B} N={N} H={H} lens={lens}: normwise o err {eo:.2e}, lse err {el:.2e}")
 
 
+@pytest.mark.parametrize("case", [
+    dict(B=2, N=8, H=4, Dl=64, Dr=32, prefix=("list", [8, 0]), tree=("chain",)),        # the tiny model's dims
+    dict(B=3, N=33, H=8, Dl=256, Dr=32, prefix=("list", [100, 0, 700]), tree=("uniform",)),
+    dict(B=1, N=5, H=3, Dl=500, Dr=12, prefix=("fixed", 40), tree=("bounded", 3, 2)),     # odd dims
+])
+def test_attn_bf16_generic_dims(case):
+    """bf16 inputs at dims other than the MFMA kernel's (512, 64) run on the generic kernel, in
+    float32 arithmetic on the same bf16 values the oracle reads: held to the fp32 bar."""
+    w = make_workload(dtype="bf16", std=0.5, scale=0.11, seed=17, **case)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, dw.max_len) == 1
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_attn(w, m_ref)
+    compare_attn(w, o, lse, o_ref, lse_ref)
+    eo = float(np.abs(o.cpu().numpy() - o_ref).max())
+    el = float(np.abs(lse.cpu().numpy() - lse_ref).max())
+    assert eo <= 1e-5 and el <= 1e-5, (eo, el)
+
+
 def _bf16_bits(x):
     from synth import bf16_bits
     return bf16_bits(np.asarray(x, np.float32))
