@@ -712,7 +712,6 @@ verify_attn_bf16_kernel(AttnArgs a) {
             mfma_s_last(sn, kf, qv);
           else
             mfma_s(sn, kf, qv);
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
 
@@ -843,7 +842,6 @@ verify_attn_bf16_kernel(AttnArgs a) {
           m_max = fmaxf(m_max, m_abs + mx);
           overflow |= mx > kHeadroomLog2;
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     pb[0] = pn[0];

@@ -1,0 +1,78 @@
+"""Compile-time check of the attention kernel's MFMA operand hazards (CPU only).
+
+The kernel issues its MFMAs through inline asm, so the compiler's hazard recognizer does not
+know they are MFMAs.  The wait states an MFMA needs after a VALU instruction writes one of
+its source VGPRs therefore rest on the instruction schedule: the P operand is produced by
+VALU code, and the register allocator may insert copies of it.  This test compiles the
+kernel to gfx950 assembly and requires at least 4 other instructions between any VALU write
+of a VGPR and an MFMA that reads it (the ISA asks for 2 wait states here).  The wait states
+the asm itself provides (after the last S^T MFMA, before the first O^T MFMA, after the tile
+loop) are written into the asm statements and need no check.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "mla_tree_verify_absorb_amd", "csrc", "verify_attn_bf16.hip")
+MIN_BETWEEN = 4
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+def _vgprs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _kernel_lines(asm, name):
+    out, inside = [], False
+    for raw in asm.splitlines():
+        line = raw.strip()
+        if re.match(rf"^_Z\S*{name}\S*:", line):
+            inside = True
+            continue
+        if inside:
+            if line.startswith("s_endpgm"):
+                break
+            if line and not line.startswith((";", ".")):
+                out.append(line)
+    return out
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_no_valu_write_close_before_an_mfma_source(tmp_path):
+    asm_path = tmp_path / "verify_attn_bf16.s"
+    subprocess.run([_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S", SRC,
+                    "-o", str(asm_path)], check=True, capture_output=True)
+    lines = _kernel_lines(asm_path.read_text(), "verify_attn_bf16_kernel")
+    assert sum(l.startswith("v_mfma") for l in lines) >= 68, "kernel not found in the assembly"
+    close = []
+    for i, line in enumerate(lines):
+        if not line.startswith("v_mfma"):
+            continue
+        srcs = set()
+        for op in line.split(None, 1)[1].split(",")[1:]:
+            srcs |= _vgprs(op.strip())
+        for back in range(1, MIN_BETWEEN + 1):
+            j = i - back
+            if j < 0:
+                break
+            prev = lines[j]
+            if prev.startswith("v_") and not prev.startswith(("v_mfma", "v_accvgpr")) and " " in prev:
+                dst = prev.split(None, 1)[1].split(",")[0].strip()
+                if _vgprs(dst) & srcs:
+                    close.append((back - 1, prev, line))
+    assert not close, f"VALU writes too close before MFMA source reads: {close[:5]}"
