@@ -37,7 +37,7 @@
 //    (one element per MFMA) in the shadow of the latter, so no softmax work
 //    sits between the two MFMA streams on the common path.
 //  * MFMAs are issued by inline asm to pin S^T to VGPRs and O^T to AGPRs;
-//    LDS fragment reads run 4 MFMAs ahead; workgroups are mapped so that a
+//    LDS fragment reads run 3-4 MFMAs ahead; workgroups are mapped so that a
 //    request's row blocks share one XCD's L2.
 //  * On tiles of the slow path (tree tiles, a partial last prefix tile, a
 //    row's first visible tile) P is applied as two bf16 terms, hi + lo, so
@@ -81,7 +81,7 @@ constexpr float kHeadroomLog2 = 100.0f;     // scores may exceed a row's referen
 constexpr bf16x2 kBf16Ones = {(__bf16)1.0f, (__bf16)1.0f};
 
 static_assert(KT * R_ROW == NWAVES * 1024, "rotary region must split into one 1 KB load per wave");
-static_assert(LOADS_PER_WAVE == 9, "the copies are spread over the first 27 S^T MFMAs (one every third)");
+static_assert(LOADS_PER_WAVE == 9, "the copies are spread over the first 33 S^T MFMAs (one every fourth)");
 
 // LDS layout of a tile.  Latent rows: key k at k * 1024, its 16-byte chunk p at
 // 16 * (p >> 4) + ((p & 15) ^ swz(k)).  gfx950's LDS has 64 banks of 4 bytes.
@@ -460,7 +460,9 @@ __device__ __forceinline__ void band_cursor_next(const AttnArgs& a, PieceCursor&
 constexpr int KRING = 4;   // K-fragment reads in flight ahead of the S^T MFMAs
 constexpr int QREG = DL / 16 - 4;   // latent query k-steps held in VGPRs; the last 4 are staged in LDS
 static_assert(DL / 16 - QREG == DR / 16, "the staged latent queries use the rotary pair-row layout");
-constexpr int VRING = 4;   // V^T-fragment reads in flight ahead of the O^T MFMAs
+constexpr int VRING = 3;   // V^T-fragment reads (pairs) in flight ahead of the O^T MFMAs
+// s_waitcnt operand: lgkmcnt(n), no vmcnt or expcnt wait
+constexpr int lgkm_wait(int n) { return 0xC07F | (n << 8); }
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 verify_attn_bf16_kernel(AttnArgs a) {
@@ -681,7 +683,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < KRING; ++s) kring[s] = *reinterpret_cast<const bf16x8*>(kbuf + kaddr(kbase, s));
         // tile tn + 1 (past the end: tile t1 - 1 again, into the free slot, so
-        // that the copies need no branch); one copy every third S^T MFMA
+        // that the copies need no branch); one copy every fourth S^T MFMA
         const CopyPlan cplan = copy_plan(a, b, p0, L, n_pt, min(tn + 1, t1 - 1));
         const uint32_t lds_d = lds0 + slot_d * TILE_BYTES;
 #pragma unroll
@@ -703,9 +705,9 @@ verify_attn_bf16_kernel(AttnArgs a) {
             qrr[nq % QRING] = *reinterpret_cast<const bf16x8*>(s_qx + part * ROWS * R_ROW + (row_local >> 1) * 256 +
                                                                (pair_chunk(row_local, cc) << 4));
           }
-          if (s % 3 == 1 && s / 3 < LOADS_PER_WAVE) issue_copy(cplan, clanes, lds_d, wave, s / 3);
-          // one LDS wait per pair of MFMAs: K fragments s and s + 1 (3 younger reads in flight)
-          if (s % 2 == 0 && s + 1 < DL / 16 + DR / 16) __builtin_amdgcn_s_waitcnt(0xC37F);
+          if (s % 4 == 1 && s / 4 < LOADS_PER_WAVE) issue_copy(cplan, clanes, lds_d, wave, s / 4);
+          // one LDS wait per pair of MFMAs: K fragments s and s + 1 (KRING - 1 younger reads in flight)
+          if (s % 2 == 0 && s + 1 < DL / 16 + DR / 16) __builtin_amdgcn_s_waitcnt(lgkm_wait(KRING - 1));
           if (s == 0)
             mfma_s_first(sn, kf, qv);
           else if (s == DL / 16 + DR / 16 - 1)
@@ -810,8 +812,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
         const int ks = st / (DL / 32), db = st % (DL / 32);
         const bf16x8 vf = vring[st % VRING];
         if (st + VRING < NST) vring[st % VRING] = load_vt(buf, voff, voff_hi, (st + VRING) / (DL / 32), (st + VRING) % (DL / 32));
-        // one LDS wait per pair of MFMAs: V^T fragments st and st + 1 (3 younger pairs in flight)
-        if (st % 2 == 0 && st + 4 < NST) __builtin_amdgcn_s_waitcnt(0xC67F);
+        // one LDS wait per pair of MFMAs: V^T fragments st and st + 1 (VRING - 1 younger pairs in flight)
+        if (st % 2 == 0 && st + 1 < NST) __builtin_amdgcn_s_waitcnt(lgkm_wait(2 * (VRING - 1)));
         if (st == 0)
           mfma_o_first(oacc[db], vf, pb[ks]);
         else
