@@ -18,10 +18,11 @@
 // both with an explicit lowest-index tie rule, so the result does not depend
 // on the reduction order.  NaN never compares greater and is never chosen.
 // accept_path: one workgroup per request, one thread per node; each thread
-// walks its ancestor chain (bounded by N) to decide whether its root path
-// matches, the deepest matching node (smallest index on ties) is found with
-// an LDS max over a packed (depth, -index) key, and the path's members place
-// themselves by depth.
+// walks its ancestor chain once (bounded by N) to decide whether its root path
+// matches and to record its ancestors as a bitmask; the deepest matching node
+// (smallest index on ties) is found with an LDS max over a packed (depth,
+// -index) key, and the nodes in the terminal's bitmask place themselves by
+// depth.
 #include <climits>
 
 #include "ddtree_internal.h"
@@ -125,9 +126,11 @@ __global__ void __launch_bounds__(256) accept_path_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ accept_len,
                                                           int32_t* __restrict__ accept_nodes,
                                                           int32_t* __restrict__ commit_tokens) {
+  constexpr int kWords = 256 / 32;
   __shared__ int s_par[256];
   __shared__ int s_tok[256];
   __shared__ int s_ts[256];
+  __shared__ uint32_t s_anc[256][kWords + 1];   // node's ancestors-or-self (padded row: no bank conflicts)
   __shared__ unsigned s_key;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -140,12 +143,19 @@ __global__ void __launch_bounds__(256) accept_path_kernel(const int32_t* __restr
   if (tid == 0) s_key = 0u;
   __syncthreads();
 
-  // Is every draft token on the root path of node tid equal to its parent's argmax?
+  // One walk up the ancestor chain of node tid: is every draft token on its root
+  // path equal to its parent's argmax, how deep is it, and which nodes are on it.
   int valid = 0, d = 0;
+  uint32_t anc[kWords];
+#pragma unroll
+  for (int w = 0; w < kWords; ++w) anc[w] = 0u;
   if (tid < N) {
     valid = 1;
     int k = tid;
-    while (k > 0 && d < N) {
+    while (true) {
+#pragma unroll
+      for (int w = 0; w < kWords; ++w) anc[w] |= (k >> 5) == w ? 1u << (k & 31) : 0u;
+      if (k == 0 || d >= N) break;
       const int p = s_par[k];
       if (p < 0 || p >= k) {        // not a tree: reject (bounded walk either way)
         valid = 0;
@@ -155,6 +165,8 @@ __global__ void __launch_bounds__(256) accept_path_kernel(const int32_t* __restr
       k = p;
       ++d;
     }
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) s_anc[tid][w] = anc[w];
     if (valid) atomicMax(&s_key, ((unsigned)d << 16) | (0xFFFFu - (unsigned)tid));
   }
   __syncthreads();
@@ -167,14 +179,10 @@ __global__ void __launch_bounds__(256) accept_path_kernel(const int32_t* __restr
       accept_nodes[base + tid] = -1;
       commit_tokens[base + tid] = -1;
     }
-    if (valid && d <= len) {
-      // ancestor of the terminal at depth d
-      int k = term;
-      for (int s = 0; s < len - d; ++s) k = s_par[k];
-      if (k == tid) {
-        accept_nodes[base + d] = tid;
-        if (d >= 1) commit_tokens[base + d - 1] = s_tok[tid];
-      }
+    // node tid is on the accepted path iff it is an ancestor-or-self of the terminal
+    if ((s_anc[term][tid >> 5] >> (tid & 31)) & 1u) {
+      accept_nodes[base + d] = tid;
+      if (d >= 1) commit_tokens[base + d - 1] = s_tok[tid];
     }
   }
   if (tid == 0) {
