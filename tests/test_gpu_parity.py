@@ -291,6 +291,36 @@ def test_attn_bf16_generic_dims(case):
     assert eo <= 1e-5 and el <= 1e-5, (eo, el)
 
 
+def test_attn_bf16_band_schedule_long_single_request():
+    """One 131072-token request, 128 nodes: its two bands (64 row blocks) are cut across all 8
+    windows, so every row is merged from pieces; sampled nodes against the oracle."""
+    params = dict(K2)
+    params.update(B=1, N=128, prefix=("fixed", 131072), tree=("bounded", 12, 4))
+    w = make_workload(seed=33, **params)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, dw.max_len) == 0
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    torch.cuda.synchronize()
+    nodes = [(0, i) for i in (0, 1, 63, 64, 127)]
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    print(f"band schedule, one 131072-token request: normwise o err {eo:.2e}, lse err {el:.2e}")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_attn_bf16_uniform_splits_on_band_shapes(splits):
+    """An explicit split count takes the uniform schedule even where the band schedule would apply."""
+    params = dict(K2)
+    params.update(B=5, N=64, prefix=("list", [3000, 0, 700, 41, 1500]), tree=("bounded", 8, 4))
+    w = make_workload(seed=34, **params)
+    dw = DevWorkload(w)
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask, num_splits=splits)
+    torch.cuda.synchronize()
+    compare_attn(w, o, lse, *oracle_attn(w, m_ref))
+
+
 def _bf16_bits(x):
     from synth import bf16_bits
     return bf16_bits(np.asarray(x, np.float32))
