@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5, help="workload number (3, 4 or 5); 5 is the headline")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="override the workload's head count (8: one GPU's share under 8-way head parallelism)")
     ap.add_argument("--splits", type=int, default=0,
                     help="uniform KV splits (0 = the library's automatic schedule)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
@@ -203,7 +205,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    w = make_config(args.config)
+    w = make_config(args.config, heads=args.heads or None)
     gen_s = time.perf_counter() - t_gen
 
     def to_dev(a):
@@ -287,7 +289,7 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": CONFIGS[args.config]["name"], "batch": w.B, "tree_nodes": w.N, "heads": w.H,
+        "config": {"workload": w.name, "batch": w.B, "tree_nodes": w.N, "heads": w.H,
                    "kv_lora": w.Dl, "rope_dim": w.Dr, "prefix_len_max": max_len,
                    "prefix_len_total": int(w.prefix_lens.sum()), "vocab": w.V, "schedule": schedule},
         "verify_steps_per_s": round(1e3 / step_ms, 2),

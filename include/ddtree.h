@@ -119,10 +119,11 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *   softmax_scale    finite scale applied to q.k (e.g. 1/sqrt(qk head dim))
  *   num_splits       0 = automatic schedule; S > 0 = S uniform KV splits per
  *                    block of 128 query rows (flash-decoding).  Automatic: when
- *                    ceil(N*H/128) is a multiple of 32, the band schedule: a
- *                    request's 128-row blocks are grouped 32 at a time, the
- *                    groups' KV tiles laid end to end and cut into 8 equal
- *                    ranges, one per XCD (32 workgroups each), so that every CU
+ *                    n_rb = ceil(N*H/128) is a multiple of 32 or divides 32,
+ *                    the band schedule: a request's 128-row blocks are grouped
+ *                    R at a time (R = 32, or R = n_rb), the groups' KV tiles
+ *                    laid end to end and cut into at most 256/R equal ranges
+ *                    of at least 8 tiles, R workgroups each, so that every CU
  *                    carries the same work however ragged the prefix lengths;
  *                    otherwise uniform splits (ddtree_verify_attn_auto_splits).
  *                    MFMA kernel only; the generic kernel ignores it.
@@ -132,7 +133,7 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *                    ddtree_verify_attn_workspace_size(...) with the same shape
  *                    and num_splits (may be NULL when that size is 0); S
  *                    splits take S*B*N*H*(Dl+1) floats, the band schedule
- *                    512*128*(Dl+1) floats plus 128 bytes (134.5 MB)
+ *                    512*128*(Dl+1) floats plus 4096 bytes (134.5 MB)
  *                    whatever B
  * bf16 inputs on the MFMA kernel need 16-byte aligned base pointers and row
  * strides that are multiples of 8 elements (INVALID_ARG otherwise) and at most

@@ -69,9 +69,10 @@ int auto_splits(bool mfma, int B, int N, int H, int64_t max_prefix_len) {
 }
 
 // The automatic schedule is the band schedule whenever a request's row blocks
-// come in whole bands of kBandRowBlocks; 0 stands for it.
+// come in whole bands of kBandRowBlocks or divide it; 0 stands for it.
 bool band_schedule_applies(bool mfma, int N, int H) {
-  return mfma && ceil_div((int64_t)N * H, kRowsPerBlock) % kBandRowBlocks == 0;
+  const int64_t n_rb = ceil_div((int64_t)N * H, kRowsPerBlock);
+  return mfma && n_rb > 0 && (n_rb % kBandRowBlocks == 0 || kBandRowBlocks % n_rb == 0);
 }
 
 int auto_schedule(bool mfma, int B, int N, int H, int64_t max_prefix_len) {
@@ -88,7 +89,8 @@ int resolve_splits(bool mfma, int B, int N, int H, int64_t max_prefix_len, int n
 size_t workspace_bytes_for(bool mfma, int B, int N, int H, int Dl, int splits) {
   if (!mfma) return 0;
   if (splits == 0)
-    return (size_t)kBandPartSlots * kRowsPerBlock * (uint64_t)(Dl + 1) * sizeof(float) + kBandWindows * 4 * sizeof(int);
+    return (size_t)kBandPartSlots * kRowsPerBlock * (uint64_t)(Dl + 1) * sizeof(float) +
+           kBandMaxWindows * 4 * sizeof(int);
   if (splits == 1) return 0;
   const uint64_t rows = (uint64_t)B * N * H;
   return (size_t)(splits * rows * (uint64_t)(Dl + 1) * sizeof(float));

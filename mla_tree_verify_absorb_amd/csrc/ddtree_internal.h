@@ -32,14 +32,15 @@ struct AttnArgs {
   const uint32_t* mask;
   float scale;
   int splits;          // >= 1 (uniform schedule)
-  int balanced;        // 1: band schedule (row blocks per request a multiple of kBandRowBlocks)
+  int balanced;        // 1: band schedule (row blocks per request a multiple or a divisor of kBandRowBlocks)
   float* o;
   float* lse;
   // uniform schedule, splits > 1: part_o [splits][B*N*H][Dl], part_lse [splits][B*N*H]
   // band schedule: part_o [kBandPartSlots][kRowsPerBlock][Dl], part_lse [kBandPartSlots][kRowsPerBlock]
   float* part_o;
   float* part_lse;
-  int* band_edges;     // band schedule: [kBandWindows][4] cut descriptors (after part_lse)
+  int* band_edges;     // band schedule: [kBandMaxWindows][4] (after part_lse): [0] the total column
+                       // count (int64) and the window count, [e] edge e's cut descriptor
 };
 
 // bf16 MFMA kernel for (Dl, Dr) = (512, 64)
@@ -47,12 +48,16 @@ constexpr int kMfmaDl = 512;
 constexpr int kMfmaDr = 64;
 constexpr int kRowsPerBlock = 128;   // query rows (node, head) per workgroup
 constexpr int kKeysPerTile = 32;     // latent KV rows per LDS tile
-// Band schedule: 32 row blocks of one request (one per CU of an XCD) form a band;
-// the bands' KV tile columns are cut into 8 equal windows, one per XCD, and each
-// workgroup of a window keeps at most one piece at each window edge.
+// Band schedule: R row blocks of one request form a band (R = 32, one per CU of
+// an XCD, when a request has a multiple of 32 row blocks; R = all of them when
+// that count divides 32).  The bands' KV tile columns are cut into at most 256 / R
+// equal windows, 32 / R per XCD, and each workgroup of a window keeps at most one
+// piece at each window edge.
 constexpr int kBandRowBlocks = 32;
-constexpr int kBandWindows = 8;
-constexpr int kBandPartSlots = 2 * kBandWindows * kBandRowBlocks;
+constexpr int kBandXcds = 8;
+constexpr int kBandWorkgroups = kBandXcds * kBandRowBlocks;   // 256, one per CU
+constexpr int kBandMaxWindows = kBandWorkgroups;               // R = 1
+constexpr int kBandPartSlots = 2 * kBandWorkgroups;
 constexpr int64_t kMaxBf16RowStride = int64_t(1) << 24;   // elements; keeps tile row offsets in 32 bits
 
 // KV-cache compaction (byte addressing; strides in bytes)

@@ -305,17 +305,20 @@ __device__ __forceinline__ int xcd_local_item(int block, int total) {
 }
 
 // ---- band schedule ----------------------------------------------------------
-// Used when a request's row blocks come in whole groups of kBandRowBlocks (32,
-// the CUs of one XCD).  Such a group is a band: its row blocks all stream the
-// request's KV, Tb = ceil(L_b / 32) + ceil(N / 32) tile columns (a row block
-// that sees fewer tree tiles skips the excess).  The bands are laid end to end
-// in (request, band) order and their columns cut into kBandWindows equal
-// windows, one per XCD.  Workgroup (window x, slot j) takes row block j of every
-// band piece in window x, so every CU carries the same number of tiles however
-// ragged the prefixes are, and the 32 workgroups of an XCD walk the same
-// columns in step (one KV stream per L2).  A band cut by a window edge leaves
-// one partial (o, lse) per window it touches, at a slot fixed by (window, slot,
-// head or tail of the window); the band combine kernel merges them.
+// Used when a request's 128-row blocks come in whole groups of 32 (one per CU
+// of an XCD), or their count R divides 32.  A band is R row blocks of one
+// request (R = 32, or all of the request's); they all stream the request's KV,
+// Tb = ceil(L_b / 32) + ceil(N / 32) tile columns (a row block that sees fewer
+// tree tiles skips the excess).  The bands are laid end to end in (request,
+// band) order and their columns cut into equal windows: 256 / R of them (32 / R
+// per XCD, window x on XCD x % 8), fewer when that would leave a window under
+// 8 columns (the surplus workgroups idle).  Workgroup (window x, slot j) takes row block
+// j of every band piece in window x, so every CU carries the same number of
+// tiles however ragged the prefixes are, and the R workgroups of a window walk
+// the same columns in step (one KV stream per window).  A band cut by a window
+// edge leaves one partial (o, lse) per window it touches, at a slot fixed by
+// (window, slot, head or tail of the window); the band combine kernel merges
+// them.
 
 __device__ __forceinline__ int64_t request_len(const int64_t* off, int b) {
   const int64_t L = off[b + 1] - off[b];
@@ -324,6 +327,11 @@ __device__ __forceinline__ int64_t request_len(const int64_t* off, int b) {
 __device__ __forceinline__ int band_tiles(const int64_t* off, int b, int ntt) {
   return (int)((request_len(off, b) + KT - 1) / KT) + ntt;
 }
+// Row blocks per band for n_rb row blocks per request.
+__device__ __forceinline__ int band_row_blocks(int n_rb) { return n_rb % kBandRowBlocks == 0 ? kBandRowBlocks : n_rb; }
+// Fewest columns in a window: bounds the pieces per band, and so the partial
+// traffic, and keeps every window non-empty.
+constexpr int kBandMinWindowColumns = 8;
 
 // Total band columns over all requests (same value in every lane).
 __device__ int64_t band_columns_total(const int64_t* off, int B, int nb, int ntt) {
@@ -365,19 +373,20 @@ __device__ int band_find(const int64_t* off, int B, int nb, int ntt, int64_t X, 
   return B;
 }
 
-__device__ __forceinline__ int64_t window_edge(int64_t C, int x) { return C * x / kBandWindows; }
+__device__ __forceinline__ int64_t window_edge(int64_t C, int x, int windows) { return C * x / windows; }
 
 // Partial slot of workgroup (window, slot): the band cut at the window's start
 // (head) or the one cut at its end (tail).  A window inside one band has only a head.
-__device__ __forceinline__ int band_part_slot(int win, int slot, bool head) {
-  return (win * kBandRowBlocks + slot) * 2 + (head ? 0 : 1);
+__device__ __forceinline__ int band_part_slot(int win, int slot, int rbb, bool head) {
+  return (win * rbb + slot) * 2 + (head ? 0 : 1);
 }
 
 struct PieceCursor {
   int b, k;          // request, band within the request
   int Tb;            // columns of request b's bands
   int nb, ntt;       // bands per request, tree tiles of a band
-  int win, slot;     // window (XCD) and row block within each band
+  int rbb;           // row blocks per band
+  int win, slot;     // window and row block within each band
   int64_t S;         // first column of request b
   int64_t X0, X1;    // the window's columns
 };
@@ -396,6 +405,7 @@ __device__ __forceinline__ PieceCursor uniform_cursor(const PieceCursor& v) {
   c.k = __builtin_amdgcn_readfirstlane(v.k);
   c.Tb = __builtin_amdgcn_readfirstlane(v.Tb);
   c.nb = __builtin_amdgcn_readfirstlane(v.nb);
+  c.rbb = __builtin_amdgcn_readfirstlane(v.rbb);
   c.ntt = __builtin_amdgcn_readfirstlane(v.ntt);
   c.win = __builtin_amdgcn_readfirstlane(v.win);
   c.slot = __builtin_amdgcn_readfirstlane(v.slot);
@@ -407,13 +417,16 @@ __device__ __forceinline__ PieceCursor uniform_cursor(const PieceCursor& v) {
 
 __device__ PieceCursor band_cursor_start(const AttnArgs& a, int n_rb, int block) {
   PieceCursor c;
-  c.win = block % kBandWindows;
-  c.slot = block / kBandWindows;
-  c.nb = n_rb / kBandRowBlocks;
+  c.rbb = band_row_blocks(n_rb);
+  const int idx = block / kBandXcds;                    // workgroup i runs on XCD i % 8
+  c.slot = idx % c.rbb;
+  c.win = (idx / c.rbb) * kBandXcds + block % kBandXcds;
+  c.nb = n_rb / c.rbb;
   c.ntt = (a.N + KT - 1) / KT;
   const int64_t C = uniform64(band_columns_total(a.prefix_offsets, a.B, c.nb, c.ntt));
-  c.X0 = window_edge(C, c.win);
-  c.X1 = window_edge(C, c.win + 1);
+  const int windows = (int)min<int64_t>(kBandWorkgroups / c.rbb, max<int64_t>(1, C / kBandMinWindowColumns));
+  c.X0 = c.win < windows ? window_edge(C, c.win, windows) : C;
+  c.X1 = c.win < windows ? window_edge(C, c.win + 1, windows) : C;
   int64_t S;
   c.b = __builtin_amdgcn_readfirstlane(band_find(a.prefix_offsets, a.B, c.nb, c.ntt, c.X0, S));
   c.S = uniform64(S);
@@ -424,21 +437,25 @@ __device__ PieceCursor band_cursor_start(const AttnArgs& a, int n_rb, int block)
     c.k = (int)((c.X0 - c.S) / c.Tb);
   }
   // Workgroup (window x > 0, slot 0) describes edge x for the combine kernel:
-  // {cut here first, request, band, windows holding head pieces}.  The band
-  // holding column X_x is cut first at x when it starts strictly inside
-  // window x - 1 (at or after X_{x-1}, before X_x).
-  if (c.slot == 0 && c.win > 0 && threadIdx.x == 0) {
-    int4 d = make_int4(0, 0, 0, 0);
-    if (c.b < a.B) {
-      const int64_t bs = c.S + (int64_t)c.k * c.Tb, be = bs + c.Tb;
-      if (bs != c.X0 && window_edge(C, c.win - 1) <= bs) {
-        unsigned heads = 0;
-        for (int x = c.win; x < kBandWindows && window_edge(C, x) < be; ++x)
-          if (window_edge(C, x) < window_edge(C, x + 1)) heads |= 1u << x;
-        d = make_int4(1, c.b, c.k, (int)heads);
+  // {cut here first, request, band, last window the band reaches}.  The band
+  // holding column X_x is cut first at x when it starts inside window x - 1
+  // (at or after X_{x-1}, before X_x).  Window 0's slot 0 stores {C, windows}.
+  if (c.slot == 0 && threadIdx.x == 0) {
+    if (c.win == 0) {
+      reinterpret_cast<int4*>(a.band_edges)[0] =
+          make_int4((int)(uint32_t)(uint64_t)C, (int)(uint32_t)((uint64_t)C >> 32), windows, 0);
+    } else {
+      int4 d = make_int4(0, 0, 0, 0);
+      if (c.win < windows && c.b < a.B) {
+        const int64_t bs = c.S + (int64_t)c.k * c.Tb, be = bs + c.Tb;
+        if (bs != c.X0 && window_edge(C, c.win - 1, windows) <= bs) {
+          int last = c.win;
+          while (last + 1 < windows && window_edge(C, last + 1, windows) < be) ++last;
+          d = make_int4(1, c.b, c.k, last);
+        }
       }
+      reinterpret_cast<int4*>(a.band_edges)[c.win] = d;
     }
-    reinterpret_cast<int4*>(a.band_edges)[c.win] = d;
   }
   return c;
 }
@@ -529,12 +546,12 @@ verify_attn_bf16_kernel(AttnArgs a) {
     int64_t bs;
     if (!band_cursor_piece(a, cur, bs)) break;
     b = cur.b;
-    rb = cur.k * kBandRowBlocks + cur.slot;
+    rb = cur.k * cur.rbb + cur.slot;
     const int64_t be = bs + cur.Tb;
     t0 = (int)(max(cur.X0, bs) - bs);
     t1 = (int)(min(cur.X1, be) - bs);
     to_part = !(bs >= cur.X0 && be <= cur.X1);   // a piece of a band cut by a window edge
-    dest0 = to_part ? (int64_t)band_part_slot(cur.win, cur.slot, bs < cur.X0) * ROWS
+    dest0 = to_part ? (int64_t)band_part_slot(cur.win, cur.slot, cur.rbb, bs < cur.X0) * ROWS
                     : (int64_t)b * n_rows + (int64_t)rb * ROWS;
     nxt = cur;
     band_cursor_next(a, nxt);
@@ -915,49 +932,74 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 }
 
 // Band schedule: merge the pieces of every band cut by a window edge.
-// Workgroup (edge e, slot j, group g) takes rows 8 g .. 8 g + 7 of row block j of
-// the band that edge e cuts first (described by the attention kernel), if any:
-// the tail piece of window e - 1 and the head pieces of the later windows the
-// band reaches.  32 threads per row, 4 float4 columns each.
+// Workgroup (pair p, group g) takes edge e = 1 + p / R and slot j = p % R (R row
+// blocks per band): if the band at edge e is cut there first (the attention
+// kernel's descriptor), rows 8 g .. 8 g + 7 of its row block j, from the tail
+// piece of window e - 1 and the head pieces of windows e .. last (no window is
+// empty).  32 threads per row, 4 float4 columns each; lane i of a row reads the
+// log-sum-exp of pieces i, i + 32, ..., so the weights need no serial loads.
 constexpr int kCombineRowsPerGroup = 8;
 constexpr int kCombineGroups = ROWS / kCombineRowsPerGroup;
+constexpr int kCombinePairs = kBandWorkgroups - 1;   // (windows - 1) * R <= 255
 
 __global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
-  const int e = 1 + (int)blockIdx.x / (kBandRowBlocks * kCombineGroups);
-  const int j = ((int)blockIdx.x / kCombineGroups) % kBandRowBlocks;
+  const int n_rows = a.N * a.H;
+  const int rbb = band_row_blocks((n_rows + ROWS - 1) / ROWS);
+  const int windows = reinterpret_cast<const int4*>(a.band_edges)[0].z;
+  const int p = (int)blockIdx.x / kCombineGroups;
   const int grp = (int)blockIdx.x % kCombineGroups;
+  if (p >= (windows - 1) * rbb) return;
+  const int e = 1 + p / rbb;
+  const int j = p % rbb;
   const int4 d = reinterpret_cast<const int4*>(a.band_edges)[e];
   if (!d.x) return;
-  const int b = d.y, kb = d.z;
-  const unsigned heads = (unsigned)d.w;
-  const int n_rows = a.N * a.H;
+  const int b = d.y, kb = d.z, n_pc = d.w - e + 2;   // pieces: window e - 1's tail, heads of e .. last
   const int rl = grp * kCombineRowsPerGroup + ((int)threadIdx.x >> 5);
-  const int r = (kb * kBandRowBlocks + j) * ROWS + rl;
+  const int r = (kb * rbb + j) * ROWS + rl;
   if (r >= n_rows) return;
-  const int tail_slot = band_part_slot(e - 1, j, false);
-  float mx = a.part_lse[tail_slot * ROWS + rl];
-  for (int x = e; x < kBandWindows; ++x)
-    if (heads >> x & 1u) mx = fmaxf(mx, a.part_lse[band_part_slot(x, j, true) * ROWS + rl]);
+  const int c0 = threadIdx.x & 31;
+  auto piece_slot = [&](int i) { return band_part_slot(e - 1 + i, j, rbb, i > 0); };
+  float mx = -INFINITY;
+  for (int i = c0; i < n_pc; i += 32) mx = fmaxf(mx, a.part_lse[piece_slot(i) * ROWS + rl]);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
   float wsum = 0.f;
   float4 acc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int c0 = threadIdx.x & 31;
-  for (int x = e - 1; x < kBandWindows; ++x) {
-    if (x >= e && !(heads >> x & 1u)) continue;
-    const int slot = x == e - 1 ? tail_slot : band_part_slot(x, j, true);
-    const float ls = a.part_lse[slot * ROWS + rl];
-    if (ls == -INFINITY) continue;
-    const float w = expf(ls - mx);
-    wsum += w;
-    const float4* src = reinterpret_cast<const float4*>(a.part_o + ((int64_t)slot * ROWS + rl) * DL);
+  for (int i0 = 0; i0 < n_pc; i0 += 32) {
+    // an empty piece (lse -inf) has o = 0 and weight 0
+    float wl = 0.f;
+    if (i0 + c0 < n_pc && mx != -INFINITY) wl = expf(a.part_lse[piece_slot(i0 + c0) * ROWS + rl] - mx);
+    float ws = wl;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float4 v = src[c0 + 32 * k];
-      acc[k].x += w * v.x;
-      acc[k].y += w * v.y;
-      acc[k].z += w * v.z;
-      acc[k].w += w * v.w;
+    for (int off = 16; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 32);
+    wsum += ws;
+    const int n = min(32, n_pc - i0);
+    // 4 pieces at a time (16 loads in flight); a piece past the end re-reads
+    // piece ii with weight 0
+    for (int ii = 0; ii < n; ii += 4) {
+      float w[4];
+      float4 v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        w[u] = __shfl(wl, ii + u, 32);
+        const bool ok = ii + u < n;
+        if (!ok) w[u] = 0.f;
+        const float4* src =
+            reinterpret_cast<const float4*>(a.part_o + ((int64_t)piece_slot(i0 + (ok ? ii + u : ii)) * ROWS + rl) * DL);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[u][k] = src[c0 + 32 * k];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[k].x += w[u] * v[u][k].x;
+          acc[k].y += w[u] * v[u][k].y;
+          acc[k].z += w[u] * v[u][k].z;
+          acc[k].w += w[u] * v[u][k].w;
+        }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -974,7 +1016,7 @@ __global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
 hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   const int n_rb = (a.N * a.H + ROWS - 1) / ROWS;
-  const int grid = a.balanced ? kBandWindows * kBandRowBlocks : a.B * n_rb * a.splits;
+  const int grid = a.balanced ? kBandWorkgroups : a.B * n_rb * a.splits;
   hipLaunchKernelGGL(verify_attn_bf16_kernel, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -991,8 +1033,7 @@ hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_band_combine(const AttnArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_band_combine_kernel, dim3((kBandWindows - 1) * kBandRowBlocks * kCombineGroups), dim3(256),
-                     0, stream, a);
+  hipLaunchKernelGGL(attn_band_combine_kernel, dim3(kCombinePairs * kCombineGroups), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

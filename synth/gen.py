@@ -252,13 +252,17 @@ def make_workload(*, B: int, N: int, H: int, Dl: int, Dr: int, dtype: str, std: 
                     logits=logits, tokens=tokens, winners=winners, V=int(V))
 
 
-def make_config(k: int, seed: Optional[int] = None) -> Workload:
-    """One of the five reference workloads; the default seed is the config number."""
+def make_config(k: int, seed: Optional[int] = None, heads: Optional[int] = None) -> Workload:
+    """One of the five reference workloads; the default seed is the config number.  heads
+    overrides the head count (e.g. 8: one GPU's share of 64 heads under 8-way head parallelism;
+    the latent KV is shared by all heads, so each GPU holds all of it)."""
     c = dict(CONFIGS[k])
-    return make_workload(B=c["B"], N=c["N"], H=c["H"], Dl=c["Dl"], Dr=c["Dr"], dtype=c["dtype"],
+    H = c["H"] if heads is None else int(heads)
+    name = c["name"] if heads is None else f"{c['name']}-h{H}"
+    return make_workload(B=c["B"], N=c["N"], H=H, Dl=c["Dl"], Dr=c["Dr"], dtype=c["dtype"],
                          std=c["std"], scale=c["scale"], prefix=c["prefix"], tree=c["tree"],
                          V=c["V"], p_match=c["p_match"], seed=k if seed is None else seed,
-                         name=c["name"])
+                         name=name)
 
 
 def restrict(w: Workload, b: int, n: int) -> Workload:

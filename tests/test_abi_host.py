@@ -127,23 +127,30 @@ def test_workspace_contract():
 
 
 # (window, slot, head/tail) partial slots of 128 rows x (Dl + 1) floats, then 8 edge descriptors of 4 ints
-BAND_WS = 2 * 8 * 32 * 128 * 513 * 4 + 8 * 16
+BAND_WS = 2 * 8 * 32 * 128 * 513 * 4 + 256 * 16
 
 
 def test_auto_schedule():
     lib = dd.lib()
-    # row blocks (128 rows each) in whole bands of 32: the band schedule (0)
+    # row blocks (128 rows each) in whole bands of 32, or a divisor of 32 of them: the band schedule (0)
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 64, 64, 512, 64, 4096) == 0       # 32 row blocks
     assert lib.ddtree_verify_attn_auto_splits(BF16, 4, 128, 64, 512, 64, 131072) == 0    # 64 per request
     assert lib.ddtree_verify_attn_auto_splits(BF16, 16, 64, 64, 512, 64, 32768) == 0
     assert lib.ddtree_verify_attn_auto_splits(BF16, 3, 32, 128, 512, 64, 10) == 0
     assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 0) == BAND_WS
     assert lib.ddtree_verify_attn_workspace_size(BF16, 16, 64, 64, 512, 64, 32768, 0) == BAND_WS
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 4096) == 0        # 4 row blocks
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 32) == 0
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 4, 128, 8, 512, 64, 131072) == 0     # 8 row blocks
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 2, 1, 8, 512, 64, 100) == 0          # one partial row block
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 16, 16, 512, 64, 4096) == 0       # 2 row blocks
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 2, 1, 8, 512, 64, 100, 0) == BAND_WS
     # otherwise uniform splits: enough workgroups to cover 256 CUs, at least 4 tiles per split
-    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 4096) == 32       # 4 row blocks, 129 tiles / 4
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 24, 64, 512, 64, 4096) == 22      # 12 row blocks: 256 / 12
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 40, 64, 512, 64, 4096) == 13      # 20 row blocks
     assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 40, 64, 512, 64, 4096, 0) == 13 * 40 * 64 * 513 * 4
-    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 8, 64, 512, 64, 32) == 1          # 2 tiles: no split
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 24, 64, 512, 64, 32) == 1         # 2 tiles: no split
+    assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 3, 128, 512, 64, 4096) == 32      # 3 row blocks: 86, capped at 129 / 4
     assert lib.ddtree_verify_attn_auto_splits(BF16, 9, 40, 64, 512, 64, 4096) == 2       # 180 row blocks
     assert lib.ddtree_verify_attn_auto_splits(F32, 1, 8, 4, 64, 32, 4096) == 1
     # bf16 away from the MFMA dims takes the generic kernel: no split, no workspace

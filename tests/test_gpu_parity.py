@@ -196,6 +196,23 @@ def test_attn_bf16_full_configs(k):
     print(f"config {k}: normwise o err {eo:.2e}, lse err {el:.2e} on {len(nodes)} nodes")
 
 
+@pytest.mark.parametrize("k", [3, 4, 5])
+def test_attn_bf16_tp8_share(k):
+    """One GPU's share of the K2 workloads under 8-way head parallelism (8 of 64 heads, the latent
+    KV replicated): 1 to 8 row blocks per request, a divisor of 32, take the band schedule with
+    bands of that many row blocks."""
+    w = make_config(k, heads=8)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, dw.max_len) == 0
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    torch.cuda.synchronize()
+    nodes = sampled_nodes(w)
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    print(f"config {k}, 8 heads: normwise o err {eo:.2e}, lse err {el:.2e} on {len(nodes)} nodes")
+
+
 def test_attn_bf16_split_invariance_and_determinism():
     """Every split count matches the oracle; a repeated call is bitwise identical (no atomics).
     Different split counts round P to bf16 against different running maxima, so they agree
@@ -268,6 +285,66 @@ def test_attn_bf16_band_schedule_random_shapes(seed):
     o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
     eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
     print(f"seed {seed}: B={B} N={N} H={H} lens={lens}: normwise o err {eo:.2e}, lse err {el:.2e}")
+
+
+@pytest.mark.parametrize("case", [
+    # 4 row blocks per request: bands of 4, 64 windows, ragged prefixes
+    dict(B=12, N=64, H=8, prefix=("list", [0, 1, 31, 32, 33, 1500, 700, 2900, 64, 5, 3100, 950]),
+         tree=("bounded", 8, 4)),
+    # 1 row block: 256 windows over 158 columns, most of them empty; the band is cut at every
+    # non-empty window's edge
+    dict(B=1, N=16, H=8, prefix=("fixed", 5000), tree=("uniform",)),
+    # 2 row blocks, the second one ragged (240 rows)
+    dict(B=3, N=30, H=8, prefix=("list", [400, 0, 2000]), tree=("bounded", 6, 3)),
+    # 16 row blocks per request, 16 windows
+    dict(B=5, N=128, H=16, prefix=("list", [3000, 0, 700, 41, 1500]), tree=("bounded", 12, 4)),
+    # more requests than one 64-lane scan chunk, 2 row blocks each
+    dict(B=70, N=16, H=16, prefix=("uniform", 0, 300), tree=("uniform",)),
+    # one node per request: 1 row block of 8 rows
+    dict(B=2, N=1, H=8, prefix=("list", [100, 0]), tree=("chain",)),
+])
+def test_attn_bf16_small_bands(case):
+    """Band schedule with fewer than 32 row blocks per request (a divisor of 32): bands of that
+    many row blocks over 256 / R windows.  Every output row, whole or merged from pieces, matches
+    the oracle; a repeated call is bitwise identical."""
+    params = dict(K2)
+    params.update(case)
+    w = make_workload(seed=37, **params)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, dw.max_len) == 0
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    o2, lse2 = dw.attn(mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    nodes = None
+    if w.B > 32:
+        nodes = [(b, i) for b in (0, 31, 63, 64, w.B - 1) for i in (0, w.N // 2, w.N - 1)]
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    print(f"small bands B={w.B} N={w.N} H={w.H}: normwise o err {eo:.2e}, lse err {el:.2e}")
+
+
+@pytest.mark.parametrize("seed", [111, 112, 114, 115, 117, 130])
+def test_attn_bf16_small_bands_random_shapes(seed):
+    """Seeded random shapes with 1 to 16 row blocks per request and a length mix of empty,
+    sub-tile and long prefixes; sampled nodes of every fourth request against the oracle."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    N, H = [(16, 8), (64, 8), (128, 8), (30, 8), (64, 16), (128, 16), (32, 32)][int(rng.integers(0, 7))]
+    lens = [int(rng.choice([0, int(rng.integers(1, 40)), int(rng.integers(40, 6000))])) for _ in range(B)]
+    params = dict(K2)
+    params.update(B=B, N=N, H=H, prefix=("list", lens), tree=("bounded", 10, 4))
+    w = make_workload(seed=seed, **params)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, dw.max_len) == 0
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    torch.cuda.synchronize()
+    nodes = [(b, i) for b in range(0, B, 4) for i in sorted({0, N // 3, N - 1})]
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    print(f"seed {seed}: B={B} N={N} H={H}: normwise o err {eo:.2e}, lse err {el:.2e}")
 
 
 @pytest.mark.parametrize("case", [
