@@ -16,9 +16,13 @@ pytestmark = pytest.mark.gpu
 K2 = dict(H=64, Dl=512, Dr=64, dtype="bf16", std=0.5, scale=1.0 / np.sqrt(192.0))
 
 
-def test_verify_step_graph_replays_match_eager():
+@pytest.mark.parametrize("heads", [64, 8])
+def test_verify_step_graph_replays_match_eager(heads):
+    """64 heads: bands of 32 row blocks over 8 windows; 8 heads: bands of 4 row blocks over 19
+    windows, the band of the 3000-token request cut at several edges."""
     params = dict(K2)
-    params.update(B=4, N=64, prefix=("list", [500, 3000, 0, 1200]), tree=("bounded", 8, 4), V=4096, p_match=0.8)
+    params.update(B=4, N=64, H=heads, prefix=("list", [500, 3000, 0, 1200]), tree=("bounded", 8, 4), V=4096,
+                  p_match=0.8)
     w = make_workload(seed=41, **params)
     dw = DevWorkload(w)
     B, N, H = w.B, w.N, w.H
