@@ -75,6 +75,19 @@ bool band_schedule_applies(bool mfma, int N, int H) {
   return mfma && n_rb > 0 && (n_rb % kBandRowBlocks == 0 || kBandRowBlocks % n_rb == 0);
 }
 
+// Most windows the band schedule may use: 256 / R, fewer when even requests of
+// max_prefix_len tokens leave under kBandMinWindowColumns columns a window.  The
+// kernel takes the smaller of this and its own count from the true lengths, so
+// a max_prefix_len below a true length costs balance, never correctness.
+int band_windows_bound(int B, int N, int H, int64_t max_prefix_len) {
+  const int64_t n_rb = ceil_div((int64_t)N * H, kRowsPerBlock);
+  const int64_t rbb = n_rb % kBandRowBlocks == 0 ? kBandRowBlocks : n_rb;
+  const int64_t cols = (int64_t)B * (n_rb / rbb) * (ceil_div(max_prefix_len, kKeysPerTile) + ceil_div(N, kKeysPerTile));
+  const int64_t w = cols / kBandMinWindowColumns;
+  const int64_t most = kBandWorkgroups / rbb;
+  return (int)(w < 1 ? 1 : (w > most ? most : w));
+}
+
 int auto_schedule(bool mfma, int B, int N, int H, int64_t max_prefix_len) {
   if (band_schedule_applies(mfma, N, H)) return 0;
   return auto_splits(mfma, B, N, H, max_prefix_len);
@@ -227,6 +240,7 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   a.part_o = nullptr;
   a.part_lse = nullptr;
   a.band_edges = nullptr;
+  a.band_windows = 0;
   if (splits > 1) {
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = a.part_o + (uint64_t)splits * rows * Dl;
@@ -234,6 +248,7 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = a.part_o + (uint64_t)kBandPartSlots * kRowsPerBlock * Dl;
     a.band_edges = reinterpret_cast<int*>(a.part_lse + (uint64_t)kBandPartSlots * kRowsPerBlock);
+    a.band_windows = band_windows_bound(B, N, H, max_prefix_len);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;

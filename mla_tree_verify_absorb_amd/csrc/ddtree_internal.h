@@ -41,6 +41,8 @@ struct AttnArgs {
   float* part_lse;
   int* band_edges;     // band schedule: [kBandMaxWindows][4] (after part_lse): [0] the total column
                        // count (int64) and the window count, [e] edge e's cut descriptor
+  int band_windows;    // band schedule: most windows (host bound from the longest prefix; the
+                       // kernel uses fewer when the columns run short)
 };
 
 // bf16 MFMA kernel for (Dl, Dr) = (512, 64)
@@ -57,6 +59,7 @@ constexpr int kBandRowBlocks = 32;
 constexpr int kBandXcds = 8;
 constexpr int kBandWorkgroups = kBandXcds * kBandRowBlocks;   // 256, one per CU
 constexpr int kBandMaxWindows = kBandWorkgroups;               // R = 1
+constexpr int kBandMinWindowColumns = 8;   // fewest KV tile columns in a window
 constexpr int kBandPartSlots = 2 * kBandWorkgroups;
 constexpr int64_t kMaxBf16RowStride = int64_t(1) << 24;   // elements; keeps tile row offsets in 32 bits
 

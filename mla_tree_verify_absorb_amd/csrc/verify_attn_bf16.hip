@@ -329,9 +329,6 @@ __device__ __forceinline__ int band_tiles(const int64_t* off, int b, int ntt) {
 }
 // Row blocks per band for n_rb row blocks per request.
 __device__ __forceinline__ int band_row_blocks(int n_rb) { return n_rb % kBandRowBlocks == 0 ? kBandRowBlocks : n_rb; }
-// Fewest columns in a window: bounds the pieces per band, and so the partial
-// traffic, and keeps every window non-empty.
-constexpr int kBandMinWindowColumns = 8;
 
 // Total band columns over all requests (same value in every lane).
 __device__ int64_t band_columns_total(const int64_t* off, int B, int nb, int ntt) {
@@ -424,7 +421,9 @@ __device__ PieceCursor band_cursor_start(const AttnArgs& a, int n_rb, int block)
   c.nb = n_rb / c.rbb;
   c.ntt = (a.N + KT - 1) / KT;
   const int64_t C = uniform64(band_columns_total(a.prefix_offsets, a.B, c.nb, c.ntt));
-  const int windows = (int)min<int64_t>(kBandWorkgroups / c.rbb, max<int64_t>(1, C / kBandMinWindowColumns));
+  // at least kBandMinWindowColumns columns a window (bounds the pieces per band,
+  // and so the partial traffic, and keeps every window non-empty)
+  const int windows = (int)min<int64_t>(a.band_windows, max<int64_t>(1, C / kBandMinWindowColumns));
   c.X0 = c.win < windows ? window_edge(C, c.win, windows) : C;
   c.X1 = c.win < windows ? window_edge(C, c.win + 1, windows) : C;
   int64_t S;
@@ -940,7 +939,6 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 // log-sum-exp of pieces i, i + 32, ..., so the weights need no serial loads.
 constexpr int kCombineRowsPerGroup = 8;
 constexpr int kCombineGroups = ROWS / kCombineRowsPerGroup;
-constexpr int kCombinePairs = kBandWorkgroups - 1;   // (windows - 1) * R <= 255
 
 __global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
   const int n_rows = a.N * a.H;
@@ -1011,6 +1009,100 @@ __global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
   if (c0 == 0) a.lse[grow] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
+// Band schedule with small bands (R < 32): a cut band has few rows and may have
+// hundreds of pieces (one request, one row block, 256 windows), so the four
+// waves of a workgroup split the pieces of 2 rows, 4 pieces at a time (16 float4
+// loads in flight per lane), with weights against the max over all the pieces;
+// the waves' sums are added through LDS.  Same (edge, slot) pairs as above, 64
+// groups of 2 rows per row block.
+constexpr int kSplitRows = 2;
+constexpr int kSplitGroups = ROWS / kSplitRows;
+
+__global__ void __launch_bounds__(256) attn_band_combine_split_kernel(AttnArgs a) {
+  __shared__ float4 s_acc[3][64][4];
+  __shared__ float s_w[3][64];
+  const int n_rows = a.N * a.H;
+  const int rbb = band_row_blocks((n_rows + ROWS - 1) / ROWS);
+  const int windows = reinterpret_cast<const int4*>(a.band_edges)[0].z;
+  const int p = (int)blockIdx.x / kSplitGroups;
+  const int grp = (int)blockIdx.x % kSplitGroups;
+  if (p >= (windows - 1) * rbb) return;
+  const int e = 1 + p / rbb;
+  const int j = p % rbb;
+  const int4 d = reinterpret_cast<const int4*>(a.band_edges)[e];
+  if (!d.x) return;
+  const int b = d.y, kb = d.z, n_pc = d.w - e + 2;   // pieces: window e - 1's tail, heads of e .. last
+  const int wave = (int)threadIdx.x >> 6;
+  const int lane = (int)threadIdx.x & 63;
+  const int rl = grp * kSplitRows + (lane >> 5);
+  const int r = (kb * rbb + j) * ROWS + rl;
+  if ((kb * rbb + j) * ROWS + grp * kSplitRows >= n_rows) return;   // the whole group is past the end
+  const bool row_ok = r < n_rows;
+  const int c0 = lane & 31;
+  auto piece_slot = [&](int i) { return band_part_slot(e - 1 + i, j, rbb, i > 0); };
+  float mx = -INFINITY;
+  for (int i = c0; i < n_pc; i += 32) mx = fmaxf(mx, a.part_lse[piece_slot(i) * ROWS + rl]);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+  float wsum = 0.f;
+  float4 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // wave w takes pieces 4 q .. 4 q + 3 for q = w, w + 4, ...; a piece past the end
+  // re-reads piece 4 q with weight 0, an empty piece (lse -inf) has o = 0 and weight 0
+  for (int i0 = 4 * wave; i0 < n_pc; i0 += 16) {
+    float w[4];
+    float4 v[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = i0 + u < n_pc;
+      const int slot = piece_slot(ok ? i0 + u : i0);
+      const float ls = a.part_lse[slot * ROWS + rl];
+      w[u] = ok && mx != -INFINITY ? expf(ls - mx) : 0.f;
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((int64_t)slot * ROWS + rl) * DL);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[u][k] = src[c0 + 32 * k];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      wsum += w[u];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[k].x += w[u] * v[u][k].x;
+        acc[k].y += w[u] * v[u][k].y;
+        acc[k].z += w[u] * v[u][k].z;
+        acc[k].w += w[u] * v[u][k].w;
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s_acc[wave - 1][lane][k] = acc[k];
+    s_w[wave - 1][lane] = wsum;
+  }
+  __syncthreads();
+  if (wave > 0 || !row_ok) return;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    wsum += s_w[q][lane];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 t = s_acc[q][lane][k];
+      acc[k].x += t.x;
+      acc[k].y += t.y;
+      acc[k].z += t.z;
+      acc[k].w += t.w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t grow = (int64_t)b * n_rows + r;
+  float4* dst = reinterpret_cast<float4*>(a.o + grow * DL);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    dst[c0 + 32 * k] = make_float4(acc[k].x * inv, acc[k].y * inv, acc[k].z * inv, acc[k].w * inv);
+  if (c0 == 0) a.lse[grow] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+}
+
 }  // namespace
 
 hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream) {
@@ -1033,7 +1125,14 @@ hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_band_combine(const AttnArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_band_combine_kernel, dim3(kCombinePairs * kCombineGroups), dim3(256), 0, stream, a);
+  const int n_rb = (a.N * a.H + ROWS - 1) / ROWS;
+  const int rbb = n_rb % kBandRowBlocks == 0 ? kBandRowBlocks : n_rb;
+  const int pairs = (a.band_windows - 1) * rbb;   // (edge, slot) pairs of the most windows the kernel can use
+  if (pairs <= 0) return hipSuccess;
+  if (rbb == kBandRowBlocks)
+    hipLaunchKernelGGL(attn_band_combine_kernel, dim3(pairs * kCombineGroups), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_band_combine_split_kernel, dim3(pairs * kSplitGroups), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

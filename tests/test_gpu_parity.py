@@ -241,6 +241,8 @@ def test_attn_bf16_split_invariance_and_determinism():
     dict(B=3, N=128, H=64, prefix=("list", [2500, 40, 900]), tree=("bounded", 12, 4)),
     # more requests than one 64-lane scan chunk (32 nodes x 128 heads)
     dict(B=66, N=32, H=128, prefix=("uniform", 0, 96), tree=("uniform",)),
+    # the node limit: 256 nodes x 64 heads = 4 bands per request, 8 mask words per row
+    dict(B=2, N=256, H=64, prefix=("list", [3000, 100]), tree=("bounded", 16, 4)),
 ])
 def test_attn_bf16_band_schedule(case):
     """The automatic band schedule (row blocks in groups of 32, KV columns cut into 8 equal
@@ -259,6 +261,8 @@ def test_attn_bf16_band_schedule(case):
     nodes = None
     if w.B > 32:
         nodes = [(b, i) for b in (0, 31, 63, 64, w.B - 1) for i in (0, w.N // 2, w.N - 1)]
+    elif w.N > 128:
+        nodes = [(b, i) for b in range(w.B) for i in (0, 1, 63, 64, 127, 128, 200, w.N - 1)]
     o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
     eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
     print(f"band schedule B={w.B} N={w.N} H={w.H}: normwise o err {eo:.2e}, lse err {el:.2e}")
@@ -345,6 +349,26 @@ def test_attn_bf16_small_bands_random_shapes(seed):
     o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
     eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
     print(f"seed {seed}: B={B} N={N} H={H}: normwise o err {eo:.2e}, lse err {el:.2e}")
+
+
+@pytest.mark.parametrize("H,max_len", [(8, 0), (8, 100), (64, 0)])
+def test_attn_bf16_band_understated_max_prefix_len(H, max_len):
+    """The band schedule's window count is bounded on the host from max_prefix_len and on the
+    device from the true lengths; a max_prefix_len below the true lengths (outside the documented
+    contract) gives fewer windows, never a wrong result."""
+    params = dict(K2)
+    params.update(B=3, N=64, H=H, prefix=("list", [2500, 40, 4000]), tree=("bounded", 8, 4))
+    w = make_workload(seed=38, **params)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, max_len) == 0
+    mask, m_ref = check_mask(dw)
+    o, lse = dd.ddtree_verify_attn(dw.q_lat, dw.q_rope, dw.ckv, dw.krope, dw.offsets, max_len, dw.ckv_tree,
+                                   dw.krope_tree, mask, w.scale, num_splits=0)
+    torch.cuda.synchronize()
+    nodes = [(b, i) for b in range(w.B) for i in (0, 21, 42, 63)]
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    print(f"H={H}, max_prefix_len {max_len}: normwise o err {eo:.2e}, lse err {el:.2e}")
 
 
 @pytest.mark.parametrize("case", [
