@@ -681,6 +681,17 @@ verify_attn_bf16_kernel(AttnArgs a) {
       }
     }
 
+    // The first VRING V^T fragments of tile t (the A operands of its first O^T
+    // MFMAs) are read during the last S^T MFMAs of tile tn, or here when there is
+    // no tile tn: slot t is complete since the previous barrier, and the O^T
+    // stream then starts without an LDS round trip.
+    constexpr int NST = 2 * (DL / 32);
+    constexpr int S_STEPS = DL / 16 + DR / 16;
+    constexpr int VT_EARLY = S_STEPS - KRING;     // first S^T step with no K read to issue
+    static_assert(VT_EARLY + VRING <= S_STEPS, "the early V^T reads fit after the last K read");
+    const unsigned char* obuf = s_kv + slot * TILE_BYTES;
+    bf16x8 vring[VRING];
+
     f32x16 sn;                    // S^T, then exponents, of tile tn
     float c, m, m_abs;
     bool lo_n = false;            // tile tn carries a second P term
@@ -703,7 +714,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
         const CopyPlan cplan = copy_plan(a, b, p0, L, n_pt, min(tn + 1, t1 - 1));
         const uint32_t lds_d = lds0 + slot_d * TILE_BYTES;
 #pragma unroll
-        for (int s = 0; s < DL / 16 + DR / 16; ++s) {
+        for (int s = 0; s < S_STEPS; ++s) {
           const bf16x8 kf = kring[s % KRING];
           const int nx = s + KRING;
           if (nx < DL / 16) {
@@ -722,14 +733,19 @@ verify_attn_bf16_kernel(AttnArgs a) {
                                                                (pair_chunk(row_local, cc) << 4));
           }
           if (s % 4 == 1 && s / 4 < LOADS_PER_WAVE) issue_copy(cplan, clanes, lds_d, wave, s / 4);
-          // one LDS wait per pair of MFMAs: K fragments s and s + 1 (KRING - 1 younger reads in flight)
-          if (s % 2 == 0 && s + 1 < DL / 16 + DR / 16) __builtin_amdgcn_s_waitcnt(lgkm_wait(KRING - 1));
+          // one LDS wait per pair of MFMAs: K fragments s and s + 1 (KRING - 1 younger reads in
+          // flight); past the last K read the compiler's own waits cover the remaining steps
+          if (s % 2 == 0 && s < VT_EARLY) __builtin_amdgcn_s_waitcnt(lgkm_wait(KRING - 1));
           if (s == 0)
             mfma_s_first(sn, kf, qv);
-          else if (s == DL / 16 + DR / 16 - 1)
+          else if (s == S_STEPS - 1)
             mfma_s_last(sn, kf, qv);
           else
             mfma_s(sn, kf, qv);
+          if (s >= VT_EARLY && s < VT_EARLY + VRING) {
+            const int st = s - VT_EARLY;
+            vring[st] = load_vt(obuf, voff, voff_hi, st / (DL / 32), st % (DL / 32));
+          }
         }
       }
 
@@ -803,6 +819,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
         lo_n = true;
       }
     } else {
+#pragma unroll
+      for (int st = 0; st < VRING; ++st) vring[st] = load_vt(obuf, voff, voff_hi, st / (DL / 32), st % (DL / 32));
       // nothing after this tile: the shadow work below evaluates to p = 0
 #pragma unroll
       for (int e = 0; e < 16; ++e) sn[e] = 0.f;
@@ -818,11 +836,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
     float pe[16];
     float mx = -INFINITY;
     {
-      const unsigned char* buf = s_kv + slot * TILE_BYTES;
-      constexpr int NST = 2 * (DL / 32);
-      bf16x8 vring[VRING];
-#pragma unroll
-      for (int st = 0; st < VRING; ++st) vring[st] = load_vt(buf, voff, voff_hi, st / (DL / 32), st % (DL / 32));
+      const unsigned char* buf = obuf;
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const int ks = st / (DL / 32), db = st % (DL / 32);
