@@ -480,6 +480,26 @@ constexpr int VRING = 3;   // V^T-fragment reads (pairs) in flight ahead of the 
 // s_waitcnt operand: lgkmcnt(n), no vmcnt or expcnt wait
 constexpr int lgkm_wait(int n) { return 0xC07F | (n << 8); }
 
+constexpr int NST = 2 * (DL / 32);         // O^T MFMAs per tile: 2 key steps x 16 dim blocks
+// O^T step st of a tile (st a constant after unrolling): the read of V^T fragment
+// st + VRING is issued first, one LDS wait covers each pair of MFMAs (VRING - 1
+// younger pairs in flight), then O^T block db += V^T fragment st . P^T of key step ks.
+__device__ __forceinline__ void o_step(f32x16 (&oacc)[DL / 32], bf16x8 (&vring)[VRING], const bf16x8 (&pb)[2],
+                                       const unsigned char* buf, int voff, int voff_hi, int st) {
+  const int ks = st / (DL / 32), db = st % (DL / 32);
+  const bf16x8 vf = vring[st % VRING];
+  if (st + VRING < NST) vring[st % VRING] = load_vt(buf, voff, voff_hi, (st + VRING) / (DL / 32), (st + VRING) % (DL / 32));
+  if (st % 2 == 0 && st + 1 < NST) __builtin_amdgcn_s_waitcnt(lgkm_wait(2 * (VRING - 1)));
+  if (st == 0)
+    mfma_o_first(oacc[db], vf, pb[ks]);
+  else
+    mfma_o(oacc[db], vf, pb[ks]);
+}
+// O^T MFMAs of tile t issued before the probabilities of tile t + 1 are prepared
+// (they need neither), so that the MFMA pipe stays busy across that code.
+constexpr int O_HEAD = 4;
+static_assert(NST - O_HEAD >= 20, "the P pipeline needs 20 O^T steps");
+
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 verify_attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char s_kv[NBUF * TILE_BYTES];
@@ -685,7 +705,6 @@ verify_attn_bf16_kernel(AttnArgs a) {
     // MFMAs) are read during the last S^T MFMAs of tile tn, or here when there is
     // no tile tn: slot t is complete since the previous barrier, and the O^T
     // stream then starts without an LDS round trip.
-    constexpr int NST = 2 * (DL / 32);
     constexpr int S_STEPS = DL / 16 + DR / 16;
     constexpr int VT_EARLY = S_STEPS - KRING;     // first S^T step with no K read to issue
     static_assert(VT_EARLY + VRING <= S_STEPS, "the early V^T reads fit after the last K read");
@@ -748,7 +767,18 @@ verify_attn_bf16_kernel(AttnArgs a) {
           }
         }
       }
+    } else {
+#pragma unroll
+      for (int st = 0; st < VRING; ++st) vring[st] = load_vt(obuf, voff, voff_hi, st / (DL / 32), st % (DL / 32));
+    }
 
+    // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row] for tile t (the pass's first
+    // iteration multiplies a zero P with the zero-filled slot 2), V^T read VRING steps
+    // ahead: the first O_HEAD steps here, the rest below with P of tile tn in their shadow.
+#pragma unroll
+    for (int st = 0; st < O_HEAD; ++st) o_step(oacc, vring, pb, obuf, voff, voff_hi, st);
+
+    if (tn < t1) {
       // ---- scores -> exponent form.  sn[4 jj + i] is key 8 jj + 4 g + i of row lr.
       // P element e is 2^(c * sn[e] - m).  Full prefix tiles, once every row has its
       // reference, use (c, m) = (scale * log2 e, m_ref) directly.  Other tiles (the
@@ -819,8 +849,6 @@ verify_attn_bf16_kernel(AttnArgs a) {
         lo_n = true;
       }
     } else {
-#pragma unroll
-      for (int st = 0; st < VRING; ++st) vring[st] = load_vt(obuf, voff, voff_hi, st / (DL / 32), st % (DL / 32));
       // nothing after this tile: the shadow work below evaluates to p = 0
 #pragma unroll
       for (int e = 0; e < 16; ++e) sn[e] = 0.f;
@@ -829,37 +857,28 @@ verify_attn_bf16_kernel(AttnArgs a) {
       m_abs = 0.f;
     }
 
-    // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row] for tile t (the pass's first
-    // iteration multiplies a zero P with the zero-filled slot 2); V^T reads VRING steps
-    // ahead.  P of tile tn (one element per MFMA), then its row max, in the shadow. ----
+    // ---- the remaining O^T steps of tile t; P of tile tn (one element per MFMA),
+    // then its row max, in their shadow. ----
     bf16x8 pn[2];
     float pe[16];
     float mx = -INFINITY;
     {
-      const unsigned char* buf = obuf;
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int ks = st / (DL / 32), db = st % (DL / 32);
-        const bf16x8 vf = vring[st % VRING];
-        if (st + VRING < NST) vring[st % VRING] = load_vt(buf, voff, voff_hi, (st + VRING) / (DL / 32), (st + VRING) % (DL / 32));
-        // one LDS wait per pair of MFMAs: V^T fragments st and st + 1 (VRING - 1 younger pairs in flight)
-        if (st % 2 == 0 && st + 1 < NST) __builtin_amdgcn_s_waitcnt(lgkm_wait(2 * (VRING - 1)));
-        if (st == 0)
-          mfma_o_first(oacc[db], vf, pb[ks]);
-        else
-          mfma_o(oacc[db], vf, pb[ks]);
+      for (int st = O_HEAD; st < NST; ++st) {
+        o_step(oacc, vring, pb, obuf, voff, voff_hi, st);
         // three-stage pipeline over the 16 elements, so that the VALU work of one
-        // step is independent: exponent of element st, 2^x and row max of st - 1,
-        // bf16 pair and exp-sum of st - 2.  The exp-sum adds the bf16-rounded
-        // values the O^T MFMAs use (one dot2 per pair), so the weights applied
-        // to V sum to exactly the normaliser.
-        if (st < 16) sn[st] = __builtin_fmaf(sn[st], c, -m);
-        if (st >= 1 && st <= 16) {
-          pe[st - 1] = __builtin_amdgcn_exp2f(sn[st - 1]);
-          mx = fmaxf(mx, sn[st - 1]);
+        // step is independent: exponent of element q, 2^x and row max of q - 1,
+        // bf16 pair and exp-sum of q - 2 (q = st - O_HEAD).  The exp-sum adds the
+        // bf16-rounded values the O^T MFMAs use (one dot2 per pair), so the weights
+        // applied to V sum to exactly the normaliser.
+        const int q = st - O_HEAD;
+        if (q < 16) sn[q] = __builtin_fmaf(sn[q], c, -m);
+        if (q >= 1 && q <= 16) {
+          pe[q - 1] = __builtin_amdgcn_exp2f(sn[q - 1]);
+          mx = fmaxf(mx, sn[q - 1]);
         }
-        if (st >= 2 && st <= 17) {
-          const int e = st - 2;
+        if (q >= 2 && q <= 17) {
+          const int e = q - 2;
           if (e & 1) {
             bf16x2 pr;
             pr[0] = (__bf16)pe[e - 1];
@@ -869,8 +888,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
             l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, kBf16Ones, l_run, false);
           }
         }
-        if (st == 18) mx = halves_max(mx);
-        if (st == 19) {
+        if (q == 18) mx = halves_max(mx);
+        if (q == 19) {
           m_max = fmaxf(m_max, m_abs + mx);
           overflow |= mx > kHeadroomLog2;
         }
