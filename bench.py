@@ -62,8 +62,15 @@ def copy_calibration(mib, steps):
 
 
 def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and blank lines are dropped, so that only a change of the
+    code itself invalidates HBM counters taken on it."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines()]
+    code = "\n".join(l for l in lines if l.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def algorithmic_work(w, depth):

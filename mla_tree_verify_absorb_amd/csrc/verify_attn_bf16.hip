@@ -34,8 +34,10 @@
 //    one rerun of the workgroup's tiles with the true row maximum.
 //  * Software pipeline: iteration t runs the S^T MFMAs of tile t + 1, then
 //    the O^T MFMAs of tile t, and computes the probabilities of tile t + 1
-//    (one element per MFMA) in the shadow of the latter, so no softmax work
-//    sits between the two MFMA streams on the common path.
+//    (one element per MFMA) in the shadow of the latter.  The first V^T
+//    reads of tile t are issued during the last S^T MFMAs, and the first
+//    O^T MFMAs ahead of the probability preparation (neither depends on
+//    tile t + 1), so the MFMA pipe does not wait between the two streams.
 //  * MFMAs are issued by inline asm to pin S^T to VGPRs and O^T to AGPRs;
 //    LDS fragment reads run 3-4 MFMAs ahead; workgroups are mapped so that a
 //    request's row blocks share one XCD's L2.
