@@ -270,3 +270,16 @@ def test_rope_tree_validation():
     assert rope(q=A + 1) == INVALID            # not element aligned
     assert rope(pos=A + 64) == INVALID         # positions overlap the rotated queries
     assert rope(k=A + 4096) == INVALID         # keys overlap the queries
+
+
+def test_bench_traffic_hash_ignores_comments_only(tmp_path):
+    """The HBM-traffic figure in the bench line is keyed to the kernel's code: comment-only edits keep the key,
+    any code edit changes it."""
+    import bench
+    src = tmp_path / "k.hip"
+    src.write_text("// header\nint f(int x) {  // trailing\n  /* block\n comment */ return x + 1;\n}\n")
+    h0 = bench.source_hash(str(src))
+    src.write_text("// another header\n\nint f(int x) {\n  return x + 1;  // changed comment\n}\n")
+    assert bench.source_hash(str(src)) == h0
+    src.write_text("int f(int x) {\n  return x + 2;\n}\n")
+    assert bench.source_hash(str(src)) != h0
