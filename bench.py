@@ -62,14 +62,14 @@ def copy_calibration(mib, steps):
 
 
 def source_hash(path):
-    """Hash of the kernel source's code: comments and blank lines are dropped, so that only a change of the
-    code itself invalidates HBM counters taken on it."""
+    """Hash of the kernel source's code: comments, blank lines and runs of whitespace are dropped, so that only
+    a change of the code itself invalidates HBM counters taken on it."""
     import re
     with open(path) as f:
         text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = [re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines()]
-    code = "\n".join(l for l in lines if l.strip())
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = [" ".join(re.sub(r"//.*$", "", l).split()) for l in text.splitlines()]
+    code = "\n".join(l for l in lines if l)
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
