@@ -180,6 +180,42 @@ def time_rope(dd, torch, w, dev, q_rope, kv_tree, positions, steps):
     return {"us_per_call": us, "rows": rows, "bytes_moved": 2 * rows * w.Dr * q_rope.element_size()}
 
 
+def reference_rates(torch, dev):
+    """Rates this GPU attains on plain library work, as context for the vendor peaks: a large dense bf16 GEMM
+    (torch.matmul, hipBLASLt) and a plain 1 GiB device-to-device copy (read + write bytes).  Neither is part of
+    the verify path."""
+    n = 8192
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    x = torch.ones(((1 << 30) // 4,), device=dev, dtype=torch.float32)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_ms(fn, reps=10):
+        for _ in range(3):
+            fn()
+        times = []
+        for _ in range(reps):
+            torch.cuda._sleep(100000)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2]
+
+    gemm_ms = best_ms(lambda: torch.matmul(a, b, out=c))
+    copy_ms = best_ms(lambda: y.copy_(x))
+    out = {"gemm_bf16_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+           "gemm_shape": [n, n, n],
+           "copy_gbps": round(2 * x.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1),
+           "copy_bytes_moved": 2 * x.numel() * 4}
+    del a, b, c, x, y
+    return out
+
+
 def traffic_for_current_kernel(launch_flops):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this kernel."""
     try:
@@ -311,6 +347,11 @@ def main():
         out["accept_hbm_gbps"] = round(gbps, 1)
         out["accept_hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
         out["compact_kv"] = time_compaction(dd, torch, w, kv_tree, acc_out[1], acc_out[2], args.steps)
+    ref = reference_rates(torch, dev)
+    roofline["frac_of_measured_gemm"] = round(attn_tflops / ref["gemm_bf16_tflops"], 4)
+    if accept_bytes:
+        out["accept_frac_of_measured_copy"] = round(out["accept_hbm_gbps"] / ref["copy_gbps"], 4)
+    out["reference_rates"] = ref
     out["build_tree"] = time_tree_builder(dd, torch, w, dev, args.steps, CONFIGS[args.config]["tree"])
     out["rope_tree"] = time_rope(dd, torch, w, dev, q_rope, kv_tree, positions, args.steps)
     if args.cpu_seconds > 0:
