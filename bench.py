@@ -231,8 +231,9 @@ def traffic_for_current_kernel(launch_flops):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding is a design note, "
-              f"not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library runs a GPU's share of the work "
+              f"(requests, heads or a prefix slice); the collectives that would join several GPUs are not implemented",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb, args.steps)

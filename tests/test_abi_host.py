@@ -283,3 +283,13 @@ def test_bench_traffic_hash_ignores_comments_only(tmp_path):
     assert bench.source_hash(str(src)) == h0
     src.write_text("int f(int x) {\n  return x + 2;\n}\n")
     assert bench.source_hash(str(src)) != h0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus above 1 exits with status 2 and a message, before touching a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
