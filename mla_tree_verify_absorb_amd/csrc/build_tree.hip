@@ -95,13 +95,18 @@ __global__ void __launch_bounds__(64) build_tree_kernel(int N, int D, int K, con
   __syncthreads();
 
   for (int n = 1; n < N; ++n) {
+    // every slot past `count` holds 0, so the lane reads all of its slots at once
+    // (independent LDS reads, one round trip) instead of looping up to `count`
+    uint64_t keys[kSlots / 64];
+#pragma unroll
+    for (int i = 0; i < kSlots / 64; ++i) keys[i] = s_key[lane + 64 * i];
     uint64_t mine = 0ull;
     int mine_slot = -1;
-    for (int e = lane; e < count; e += 64) {
-      const uint64_t k = s_key[e];
-      if (k > mine) {
-        mine = k;
-        mine_slot = e;
+#pragma unroll
+    for (int i = 0; i < kSlots / 64; ++i) {
+      if (keys[i] > mine) {
+        mine = keys[i];
+        mine_slot = lane + 64 * i;
       }
     }
     // best > 0: the frontier cannot run dry before N nodes (the host checks the candidate tree's size)
