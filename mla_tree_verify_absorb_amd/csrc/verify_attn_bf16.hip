@@ -156,26 +156,39 @@ struct CopyPlan {
   int count;                // valid keys (1..32)
 };
 
+// Row indices and byte strides fit in 32 bits for any cache that fits in device
+// memory (a latent row holds 1 KB; row strides are checked below 2^24 elements on
+// the host), so each row address is one 32 x 32 -> 64-bit scalar product.
 __device__ __forceinline__ CopyPlan copy_plan(const AttnArgs& a, int b, int64_t p0, int64_t L, int n_pt, int t) {
   CopyPlan q;
+  const unsigned char* cb;
+  const unsigned char* rb;
+  uint32_t row0, cs, rs;
   if (t < n_pt) {
-    const int64_t row0 = p0 + (int64_t)t * KT;
-    q.c = static_cast<const unsigned char*>(a.ckv) + row0 * a.ld_ckv * 2;
-    q.r = static_cast<const unsigned char*>(a.krope) + row0 * a.ld_krope * 2;
-    q.cstride = (uint32_t)(a.ld_ckv * 2);
-    q.rstride = (uint32_t)(a.ld_krope * 2);
-    const int64_t rem = L - (int64_t)t * KT;
-    q.count = rem < KT ? (int)rem : KT;
+    row0 = (uint32_t)p0 + (uint32_t)t * KT;
+    cb = static_cast<const unsigned char*>(a.ckv);
+    rb = static_cast<const unsigned char*>(a.krope);
+    cs = (uint32_t)a.ld_ckv * 2u;
+    rs = (uint32_t)a.ld_krope * 2u;
+    const int rem = (int)L - t * KT;
+    q.count = rem < KT ? rem : KT;
   } else {
     const int node0 = (t - n_pt) * KT;
-    const int64_t row0 = (int64_t)b * a.N + node0;
-    q.c = static_cast<const unsigned char*>(a.ckv_tree) + row0 * a.ld_ckv_tree * 2;
-    q.r = static_cast<const unsigned char*>(a.krope_tree) + row0 * a.ld_krope_tree * 2;
-    q.cstride = (uint32_t)(a.ld_ckv_tree * 2);
-    q.rstride = (uint32_t)(a.ld_krope_tree * 2);
+    row0 = (uint32_t)(b * a.N + node0);
+    cb = static_cast<const unsigned char*>(a.ckv_tree);
+    rb = static_cast<const unsigned char*>(a.krope_tree);
+    cs = (uint32_t)a.ld_ckv_tree * 2u;
+    rs = (uint32_t)a.ld_krope_tree * 2u;
     const int rem = a.N - node0;
     q.count = rem < KT ? rem : KT;
   }
+  row0 = __builtin_amdgcn_readfirstlane(row0);   // wave-uniform: keep the products scalar
+  cs = __builtin_amdgcn_readfirstlane(cs);
+  rs = __builtin_amdgcn_readfirstlane(rs);
+  q.cstride = cs;
+  q.rstride = rs;
+  q.c = cb + (uint64_t)row0 * cs;
+  q.r = rb + (uint64_t)row0 * rs;
   return q;
 }
 
