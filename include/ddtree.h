@@ -110,7 +110,9 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *                    (the usual fused cache [T, Dl+Dr] is krope = ckv + Dl, both
  *                    ld = Dl + Dr)
  *   prefix_offsets   device int64 [B + 1]: request b owns rows offsets[b] ..
- *                    offsets[b+1]-1 (lengths may be 0)
+ *                    offsets[b+1]-1 (lengths may be 0); the MFMA kernel indexes
+ *                    rows with 32 bits, so offsets[B] < 2^32 (any cache that fits
+ *                    in device memory: a latent row alone is 1 KB there)
  *   max_prefix_len   host value >= every L_b; only used to plan the KV split
  *   ckv_tree, ld_ckv_tree      device tree-node latent rows: node (b,i) at
  *                              ckv_tree + (b*N + i)*ld_ckv_tree
