@@ -111,22 +111,19 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
-// One direct-to-LDS 16-byte load per lane: LDS[lds_base + 16 * lane] <- gbase[voff].
-// Written as inline asm so that the compiler does not treat it as an LDS store
-// and serialise every later LDS read behind it; completion is tracked by the
+// Direct-to-LDS 16-byte loads (global_load_lds_dwordx4, below) are written as
+// inline asm so that the compiler does not treat them as LDS stores and
+// serialise every later LDS read behind them; completion is tracked by the
 // explicit vmcnt waits in the tile loop (vmcnt counts every vector memory op
 // in issue order, so waits the compiler adds for its own loads stay correct).
-// M0 is written and consumed inside the one statement; nothing else in this
-// kernel uses M0.
-__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gbase, uint32_t voff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds_base), "v"(voff), "s"(gbase)
-      : "memory");
-}
+// Each statement writes M0 and declares it clobbered.  M0 is a reserved register
+// to the compiler, which does not keep values in it across statements (it
+// writes M0 right before each instruction that reads it), so clang warns that
+// the clobber is not needed for preservation; the warning is silenced here.  A
+// compile-time test checks that no other instruction of the kernel reads or
+// writes M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 
 // Wait for every tile copy this wave has issued.
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -206,7 +203,7 @@ __device__ __forceinline__ void lds_dma16_latent(uint32_t lds_base, const void* 
       "global_load_lds_dwordx4 %0, %5"
       : "=&v"(addr)
       : "s"(lds_base), "v"(lw), "i"(XR), "s"(rowoff), "s"(gbase)
-      : "memory");
+      : "memory", "m0");
 }
 // Rotary copy: lane address rowoff + piece.
 __device__ __forceinline__ void lds_dma16_rotary(uint32_t lds_base, const void* gbase, uint32_t rowoff, uint32_t piece) {
@@ -217,8 +214,10 @@ __device__ __forceinline__ void lds_dma16_rotary(uint32_t lds_base, const void* 
       "global_load_lds_dwordx4 %0, %4"
       : "=&v"(addr)
       : "s"(lds_base), "v"(rowoff), "v"(piece), "s"(gbase)
-      : "memory");
+      : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 template <int I>
 __device__ __forceinline__ void issue_copy(const CopyPlan& q, const CopyLanes& cl, uint32_t lds_buf, int wave) {

@@ -259,20 +259,22 @@ def build_tree_ref(root_tokens, cand_tokens, cand_logp, N):
     Created"; [Truth] opening.  They give no further detail; the reading
     below is the plainest one.)
 
-    Reading: depth d (1..D) offers K proposals (token, log-probability), the
-    log-probabilities non-increasing along K.  Any node at depth d-1 may take
-    any depth-d proposal as a child; a node's score is its parent's score plus
-    the proposal's log-probability (float32, added root to leaf), the root
-    scoring 0.  Nodes are taken in order of the key (score descending, then
-    depth, parent index and proposal rank ascending) until N nodes exist.  A
-    max-heap holds the frontier; after taking node (parent p, depth d, rank
-    j) it receives the next sibling (p, d, j + 1) and the first child
-    (new node, d + 1, 0).  Taken nodes are numbered in order, so every parent
-    precedes its children.
+    Reading: depth d (1..D) offers K proposals (token, log-probability).  Any
+    node at depth d-1 may take any depth-d proposal as a child; a node's score
+    is its parent's score plus the proposal's log-probability (float32, added
+    root to leaf), the root scoring 0.  Starting from the root, each step
+    looks at every child of every node taken so far that is not taken yet,
+    and takes the best one under the key (score descending, then depth,
+    parent index and proposal rank ascending), until N nodes exist.  Taken
+    nodes are numbered in order, so every parent precedes its children.
+
+    This is the definition written out: every step scans the whole frontier
+    (no heap, no lazily grown frontier).  With log-probabilities <= 0 a child
+    never outranks its parent, so the result is the root plus the N-1 best
+    nodes of the whole candidate tree.
 
     Returns parents, tokens, depth (int32 [B, N]) and scores (float32 [B, N]).
     """
-    import heapq
     root_tokens = np.asarray(root_tokens)
     cand_tokens = np.asarray(cand_tokens)
     cand_logp = np.asarray(cand_logp, dtype=np.float32)
@@ -283,21 +285,25 @@ def build_tree_ref(root_tokens, cand_tokens, cand_logp, N):
     scores = np.zeros((B, N), np.float32)
     for b in range(B):
         tokens[b, 0] = root_tokens[b]
-        node_score = [np.float32(0.0)]
-        heap = [(-(np.float32(0.0) + cand_logp[b, 0, 0]), 1, 0, 0)]
-        n = 1
-        while n < N and heap:
-            neg, d, p, j = heapq.heappop(heap)
-            s = np.float32(-neg)
-            parents[b, n], tokens[b, n], depth[b, n], scores[b, n] = p, cand_tokens[b, d - 1, j], d, s
-            node_score.append(s)
-            if j + 1 < K:
-                heapq.heappush(heap, (-(node_score[p] + cand_logp[b, d - 1, j + 1]), d, p, j + 1))
-            if d < D:
-                heapq.heappush(heap, (-(s + cand_logp[b, d, 0]), d + 1, n, 0))
-            n += 1
-        if n < N:
-            raise ValueError(f"request {b}: only {n} nodes can be built from {D} depths of {K} proposals")
+        taken = np.zeros((N, K), dtype=bool)     # taken[p, j]: child j of node p is a node already
+        for n in range(1, N):
+            # every child (p, j) of the n nodes taken so far: its score, depth, parent and rank
+            p_idx = np.repeat(np.arange(n), K)
+            j_idx = np.tile(np.arange(K), n)
+            p_depth = depth[b, p_idx]
+            open_ = (p_depth < D) & ~taken[p_idx, j_idx]
+            if not open_.any():
+                raise ValueError(f"request {b}: only {n} nodes can be built from {D} depths of {K} proposals")
+            p_idx, j_idx, p_depth = p_idx[open_], j_idx[open_], p_depth[open_]
+            child = scores[b, p_idx] + cand_logp[b, p_depth, j_idx]       # float32 additions
+            # the key's best: highest score, then lowest depth, parent, rank (lexsort: last key first)
+            best = np.lexsort((j_idx, p_idx, p_depth, -child.astype(np.float64)))[0]
+            p, j = int(p_idx[best]), int(j_idx[best])
+            taken[p, j] = True
+            parents[b, n] = p
+            tokens[b, n] = cand_tokens[b, depth[b, p], j]
+            depth[b, n] = depth[b, p] + 1
+            scores[b, n] = child[best]
     return parents, tokens, depth, scores
 
 

@@ -279,6 +279,19 @@ def restrict(w: Workload, b: int, n: int) -> Workload:
                     winners=None if w.winners is None else w.winners[b:b + 1, :n], V=w.V)
 
 
+def make_accept_draws(*, B: int, N: int, V: int, seed: int = 0):
+    """Unplanted accept inputs: logits N(0,1) float32 [B, N, V] with no planted winner (the top two of a
+    row sit close together, as in a real vocabulary), match coin flips U(0,1) [B, N], and uniform draws
+    in [0, V-1) [B, N] for mismatched tokens.  Turning these into draft tokens needs the parent's argmax,
+    which this module never computes: the caller derives the tokens from its own argmax.
+    Draw order: logits, coin flips, mismatch draws."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal(size=(B, N, V), dtype=np.float32)
+    coins = rng.random(size=(B, N))
+    other = rng.integers(0, max(V - 1, 1), size=(B, N)).astype(np.int64)
+    return logits, coins, other
+
+
 # ----------------------------------------------------------------------------
 # drafter candidates for the best-first tree builder
 # ----------------------------------------------------------------------------

@@ -12,6 +12,10 @@ from synth import Workload
 DEV = "cuda:0"
 FP32_ABS_TOL = 1e-5        # fp32 inputs: max abs error on o and lse
 BF16_NORM_TOL = 2e-3       # bf16 inputs: max|err| / max|ref| on o and lse
+# bf16 inputs, K2 workloads: max |lse - lse_ref| in nats.  Below the 2.4e-4 that leaving out (or doubling)
+# one 32-key tile of a 131072-key row would cause (ln(1 - 32/131072)), so such a mistake fails here even
+# though it passes the normwise bound.
+BF16_LSE_ABS_TOL = 1.5e-4
 
 
 def t_dev(arr: np.ndarray, dtype: str) -> torch.Tensor:
@@ -55,6 +59,15 @@ def oracle_attn(w: Workload, mask_u32: np.ndarray, nodes=None):
 
 def mask_np(mask_t: torch.Tensor) -> np.ndarray:
     return mask_t.cpu().numpy().view(np.uint32)
+
+
+def lse_abs_err(lse, lse_ref, nodes=None):
+    """max |lse - lse_ref| (nats) over all rows, or the sampled nodes' rows."""
+    lse = lse.cpu().numpy().astype(np.float64)
+    if nodes is not None:
+        bi = tuple(np.array([b for b, _ in nodes])), tuple(np.array([i for _, i in nodes]))
+        lse, lse_ref = lse[bi], lse_ref[bi]
+    return float(np.abs(lse - lse_ref).max())
 
 
 def compare_attn(w: Workload, o, lse, o_ref, lse_ref, nodes=None):

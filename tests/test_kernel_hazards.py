@@ -8,6 +8,10 @@ kernel to gfx950 assembly and requires at least 4 other instructions between any
 of a VGPR and an MFMA that reads it (the ISA asks for 2 wait states here).  The wait states
 the asm itself provides (after the last S^T MFMA, before the first O^T MFMA, after the tile
 loop) are written into the asm statements and need no check.
+
+The tile copies (direct-to-LDS loads) also live in inline asm, each writing M0 right before
+its load.  The second test requires that nothing else in the kernel reads or writes M0, so
+that a compiler-generated M0 value can never be live across one of those statements.
 """
 import os
 import re
@@ -51,13 +55,35 @@ def _kernel_lines(asm, name):
     return out
 
 
+_ASM = {}
+
+
+def _kernel_asm(tmp_path_factory):
+    if "lines" not in _ASM:
+        asm_path = tmp_path_factory.mktemp("asm") / "verify_attn_bf16.s"
+        subprocess.run([_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+                        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S", SRC,
+                        "-o", str(asm_path)], check=True, capture_output=True)
+        _ASM["lines"] = _kernel_lines(asm_path.read_text(), "verify_attn_bf16_kernel")
+    return _ASM["lines"]
+
+
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
-def test_no_valu_write_close_before_an_mfma_source(tmp_path):
-    asm_path = tmp_path / "verify_attn_bf16.s"
-    subprocess.run([_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
-                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S", SRC,
-                    "-o", str(asm_path)], check=True, capture_output=True)
-    lines = _kernel_lines(asm_path.read_text(), "verify_attn_bf16_kernel")
+def test_m0_is_written_only_by_the_tile_copies(tmp_path_factory):
+    lines = _kernel_asm(tmp_path_factory)
+    uses = [(i, l) for i, l in enumerate(lines) if re.search(r"\bm0\b", l)]
+    assert uses, "kernel not found in the assembly"
+    for i, line in uses:
+        # s_mov_b32 m0, <sgpr>; v_xad_u32 / v_add_u32 (the lane address); global_load_lds_dwordx4
+        assert re.match(r"s_mov_b32 m0, s\d+$", line), line
+        assert lines[i + 1].startswith(("v_xad_u32", "v_add_u32")), lines[i + 1]
+        assert lines[i + 2].startswith("global_load_lds_dwordx4"), lines[i + 2]
+    assert len(uses) == sum(l.startswith("global_load_lds_dwordx4") for l in lines)
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_no_valu_write_close_before_an_mfma_source(tmp_path_factory):
+    lines = _kernel_asm(tmp_path_factory)
     assert sum(l.startswith("v_mfma") for l in lines) >= 68, "kernel not found in the assembly"
     close = []
     for i, line in enumerate(lines):

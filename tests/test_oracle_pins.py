@@ -727,6 +727,34 @@ def test_tree_builder_structure(seed):
         assert ok[0] == 1 and (dep[0] == depth[b]).all()
 
 
+def level_order_scores(cand_logp):
+    """float32 scores of every node of a request's candidate tree, level by level (a node's score is
+    its parent's plus the proposal's log-probability), with the depth of each."""
+    D, K = cand_logp.shape
+    level = np.zeros(1, np.float32)
+    scores, depths = [], []
+    for d in range(D):
+        level = (level[:, None] + cand_logp[d][None, :]).reshape(-1)      # float32 additions
+        scores.append(level)
+        depths.append(np.full(level.shape, d + 1))
+    return np.concatenate(scores), np.concatenate(depths)
+
+
+@pytest.mark.parametrize("seed,D,K,N", [(0, 8, 3, 256), (1, 7, 4, 128), (2, 4, 8, 200), (3, 3, 16, 256),
+                                        (4, 12, 2, 128)])
+def test_tree_builder_takes_the_best_of_the_whole_candidate_tree(seed, D, K, N):
+    """With log-probabilities <= 0, the N-1 taken nodes are the N-1 best (score descending, then depth) of
+    the whole candidate tree, enumerated level by level and sorted; so the taken scores and depths, in
+    order, equal that sorted list's head.  Sizes up to 256 nodes, depth 12, 16 proposals."""
+    c = make_draft_candidates(B=2, D=D, K=K, V=4000, seed=seed)
+    _, _, depth, scores = build_tree_ref(c.root_tokens, c.cand_tokens, c.cand_logp, N)
+    for b in range(2):
+        all_s, all_d = level_order_scores(c.cand_logp[b])
+        order = np.lexsort((all_d, -all_s.astype(np.float64)))[:N - 1]
+        np.testing.assert_array_equal(scores[b, 1:], all_s[order])
+        np.testing.assert_array_equal(depth[b, 1:], all_d[order])
+
+
 def tree_is_valid_np(p):
     return p[0] == -1 and all(0 <= p[i] < i for i in range(1, len(p)))
 

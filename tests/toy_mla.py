@@ -27,27 +27,42 @@ import torch
 import mla_tree_verify_absorb_amd as dd
 
 
+def toy_weights(seed=0, hidden=256, layers=4, heads=4, kv_lora=64, d_nope=32, d_rope=32, d_v=32, ffn=512,
+                vocab=512):
+    """The seeded float32 weights of the toy model, on the CPU (shared by the GPU model and its float64 twin)."""
+    g = torch.Generator().manual_seed(seed)
+
+    def w(*shape, scale=None):
+        s = scale if scale is not None else 1.0 / math.sqrt(shape[-2] if len(shape) > 1 else shape[-1])
+        return torch.randn(*shape, generator=g) * s
+
+    embed = w(vocab, hidden, scale=1.0)
+    per_layer = []
+    for _ in range(layers):
+        per_layer.append(dict(
+            wq=w(hidden, heads * (d_nope + d_rope)), wdkv=w(hidden, kv_lora + d_rope),
+            wuk=w(heads, d_nope, kv_lora), wuv=w(heads, kv_lora, d_v), wo=w(heads * d_v, hidden),
+            wg=w(hidden, ffn), wu=w(hidden, ffn), wd=w(ffn, hidden)))
+    lm_head = w(hidden, vocab)
+    return dict(embed=embed, layers=per_layer, lm_head=lm_head)
+
+
+def toy_inv_freq(d_rope=32, base=10000.0):
+    """Rotary frequencies base^(-2i/d), float64."""
+    return base ** (-np.arange(0, d_rope, 2, dtype=np.float64) / d_rope)
+
+
 class ToyMLA:
     def __init__(self, seed=0, hidden=256, layers=4, heads=4, kv_lora=64, d_nope=32, d_rope=32, d_v=32, ffn=512,
                  vocab=512, capacity=512, device="cuda:0"):
-        g = torch.Generator().manual_seed(seed)
-
-        def w(*shape, scale=None):
-            s = scale if scale is not None else 1.0 / math.sqrt(shape[-2] if len(shape) > 1 else shape[-1])
-            return (torch.randn(*shape, generator=g) * s).to(device)
-
+        wts = toy_weights(seed, hidden, layers, heads, kv_lora, d_nope, d_rope, d_v, ffn, vocab)
         self.H, self.Dl, self.Dr, self.dn, self.dv, self.V = heads, kv_lora, d_rope, d_nope, d_v, vocab
         self.dev = device
-        self.embed = w(vocab, hidden, scale=1.0)
-        self.layers = []
-        for _ in range(layers):
-            self.layers.append(dict(
-                wq=w(hidden, heads * (d_nope + d_rope)), wdkv=w(hidden, kv_lora + d_rope),
-                wuk=w(heads, d_nope, kv_lora), wuv=w(heads, kv_lora, d_v), wo=w(heads * d_v, hidden),
-                wg=w(hidden, ffn), wu=w(hidden, ffn), wd=w(ffn, hidden)))
-        self.lm_head = w(hidden, vocab)
+        self.embed = wts["embed"].to(device)
+        self.layers = [{k: v.to(device) for k, v in p.items()} for p in wts["layers"]]
+        self.lm_head = wts["lm_head"].to(device)
         self.scale = 1.0 / math.sqrt(d_nope + d_rope)
-        self.inv_freq = torch.from_numpy(10000.0 ** (-np.arange(0, d_rope, 2, dtype=np.float64) / d_rope)).to(device)
+        self.inv_freq = torch.from_numpy(toy_inv_freq(d_rope)).to(device)
         # one [capacity, Dl + Dr] latent cache per layer
         self.cache = [torch.zeros((capacity, kv_lora + d_rope), dtype=torch.float32, device=device)
                       for _ in range(layers)]
