@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--splits", type=int, default=0,
                     help="uniform KV splits (0 = the library's automatic schedule)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the attention-only timings of workloads 3 and 4 in the default run")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times (HBM counter calibration)")
     return ap.parse_args()
@@ -97,9 +99,11 @@ def cpu_baseline(w, budget_s):
     from synth import restrict
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+        blas_name = ",".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in blas})) or None
     except Exception:
-        threads = os.cpu_count() or 1
+        threads, blas_name = os.cpu_count() or 1, None
     f = w.f32
     kv = f("kv")
     kt = f("kv_tree")
@@ -122,7 +126,20 @@ def cpu_baseline(w, budget_s):
     return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"request 0, tree nodes 0..{n_done - 1} one at a time (all {w.H} heads), full "
                       f"{int(w.prefix_lens[0])}-token prefix, float64 NumPy; {elapsed:.1f} s of oracle time",
-            "seconds": round(elapsed, 2)}
+            "seconds": round(elapsed, 2), "host_cpus": os.cpu_count(), "blas_threads": int(threads),
+            "blas": blas_name, "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name (first /proc/cpuinfo entry)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def gpu_time_us(torch, dev, fn, steps):
@@ -208,11 +225,79 @@ def reference_rates(torch, dev):
 
     gemm_ms = best_ms(lambda: torch.matmul(a, b, out=c))
     copy_ms = best_ms(lambda: y.copy_(x))
+    # the library's own probes: back-to-back bf16 MFMAs on every SIMD, and a read-only stream of 2 GiB
+    from mla_tree_verify_absorb_amd import rates
+    wgs, iters = 512, 40000                       # two waves per SIMD on 256 CUs
+    sink = torch.empty((wgs * 4,), dtype=torch.float32, device=dev)
+    mfma_flops = rates.mfma_loop(wgs, iters, sink)
+    mfma_ms = best_ms(lambda: rates.mfma_loop(wgs, iters, sink), reps=5)
+    rd_wgs = 256 * 8
+    rsink = torch.empty((rd_wgs * 256,), dtype=torch.int32, device=dev)
+    buf = torch.ones(((2 << 30) // 4,), dtype=torch.float32, device=dev)
+    rd_bytes = rates.stream_read(buf, rd_wgs, rsink)
+    rd_ms = best_ms(lambda: rates.stream_read(buf, rd_wgs, rsink))
     out = {"gemm_bf16_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
            "gemm_shape": [n, n, n],
            "copy_gbps": round(2 * x.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1),
-           "copy_bytes_moved": 2 * x.numel() * 4}
-    del a, b, c, x, y
+           "copy_bytes_moved": 2 * x.numel() * 4,
+           "mfma_loop_bf16_tflops": round(mfma_flops / (mfma_ms * 1e-3) / 1e12, 1),
+           "mfma_loop": f"{wgs} workgroups x 4 waves, {iters} iterations of 4 independent "
+                        f"v_mfma_f32_32x32x16_bf16 per wave, median of 5",
+           "stream_read_gbps": round(rd_bytes / (rd_ms * 1e-3) / 1e9, 1),
+           "stream_read_bytes": rd_bytes}
+    del a, b, c, x, y, buf
+    return out
+
+
+def attention_only(dd, torch, dev, k, steps, warmup):
+    """Mask + attention of workload k (its full shape, the automatic schedule) timed like the main step:
+    HIP events around the attention call (attention kernel and split merge) on its stream."""
+    import numpy as np
+    from synth import make_config
+    w = make_config(k)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    parents = torch.from_numpy(w.parents).to(dev)
+    offsets = torch.from_numpy(w.prefix_offsets).to(dev)
+    q_lat, q_rope = to_dev(w.q_lat), to_dev(w.q_rope)
+    kv, kv_tree = to_dev(w.kv), to_dev(w.kv_tree)
+    max_len = int(w.prefix_lens.max())
+    splits = dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, max_len)
+    ws = torch.empty((max(dd.ddtree_verify_attn_workspace_size(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, max_len,
+                                                               splits), 1),), dtype=torch.uint8, device=dev)
+    mask, depth, _, ok = dd.ddtree_build_mask(parents, offsets)
+    o = torch.empty((w.B, w.N, w.H, w.Dl), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.N, w.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def attn():
+        dd.ddtree_verify_attn(q_lat, q_rope, kv[:, :w.Dl], kv[:, w.Dl:], offsets, max_len, kv_tree[..., :w.Dl],
+                              kv_tree[..., w.Dl:], mask, w.scale, num_splits=splits, o=o, lse=lse, workspace=ws)
+
+    for _ in range(warmup):
+        attn()
+    torch.cuda.synchronize()
+    total = 0.0
+    for _ in range(steps):
+        torch.cuda._sleep(100000)                     # keep host launch latency out of the event interval
+        e0.record(stream)
+        attn()
+        e1.record(stream)
+        e1.synchronize()
+        total += e0.elapsed_time(e1)
+    assert int(ok.min()) == 1 and bool(torch.isfinite(o).all())
+    attn_ms = total / steps
+    flops, attn_bytes, _ = algorithmic_work(w, depth.cpu().numpy())
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    out = {"batch": w.B, "tree_nodes": w.N, "heads": w.H, "prefix_len_total": int(w.prefix_lens.sum()),
+           "prefix_len_max": max_len, "schedule": "band" if splits == 0 else f"uniform-{splits}",
+           "attn_ms": round(attn_ms, 4), "attn_tflops": round(tflops, 2),
+           "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops,
+           "algorithmic_bytes": attn_bytes, "workspace_bytes": ws.numel()}
+    del q_lat, q_rope, kv, kv_tree, o, lse, ws
     return out
 
 
@@ -348,10 +433,17 @@ def main():
         out["accept_hbm_gbps"] = round(gbps, 1)
         out["accept_hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
         out["compact_kv"] = time_compaction(dd, torch, w, kv_tree, acc_out[1], acc_out[2], args.steps)
+    if args.config == 5 and args.heads == 0 and args.splits == 0 and not args.no_other_workloads:
+        out["other_workloads"] = {CONFIGS[k]["name"]: attention_only(dd, torch, dev, k, args.steps, args.warmup)
+                                  for k in (3, 4)}
     ref = reference_rates(torch, dev)
     roofline["frac_of_measured_gemm"] = round(attn_tflops / ref["gemm_bf16_tflops"], 4)
+    roofline["frac_of_measured_mfma_loop"] = round(attn_tflops / ref["mfma_loop_bf16_tflops"], 4)
     if accept_bytes:
         out["accept_frac_of_measured_copy"] = round(out["accept_hbm_gbps"] / ref["copy_gbps"], 4)
+        out["accept_frac_of_measured_stream_read"] = round(out["accept_hbm_gbps"] / ref["stream_read_gbps"], 4)
+    for sub in out.get("other_workloads", {}).values():
+        sub["frac_of_measured_mfma_loop"] = round(sub["attn_tflops"] / ref["mfma_loop_bf16_tflops"], 4)
     out["reference_rates"] = ref
     out["build_tree"] = time_tree_builder(dd, torch, w, dev, args.steps, CONFIGS[args.config]["tree"])
     out["rope_tree"] = time_rope(dd, torch, w, dev, q_rope, kv_tree, positions, args.steps)

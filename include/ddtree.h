@@ -59,6 +59,11 @@ typedef enum {
 /* Human-readable name of a status code (static storage). */
 const char* ddtree_status_string(int status);
 
+/* Digest of the sources and flags the library was built from (16 hex digits,
+ * static storage): the binding compares it with the sources it ships with and
+ * refuses a library built from other sources. */
+const char* ddtree_build_digest(void);
+
 /*
  * ddtree_build_mask -- ancestor-or-self visibility mask, depth and positions.
  *
@@ -132,11 +137,16 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *   o                device float32 [B, N, H, Dl]
  *   lse              device float32 [B, N, H] (natural log)
  *   workspace        device scratch of workspace_bytes >=
- *                    ddtree_verify_attn_workspace_size(...) with the same shape
- *                    and num_splits (may be NULL when that size is 0); S
- *                    splits take S*B*N*H*(Dl+1) floats, the band schedule
- *                    512*128*(Dl+1) floats plus 4096 bytes (134.5 MB)
- *                    whatever B
+ *                    ddtree_verify_attn_workspace_size(...) with the same shape,
+ *                    max_prefix_len and num_splits (may be NULL when that size
+ *                    is 0); S splits take S*B*N*H*(Dl+1) floats, the band
+ *                    schedule 2*W*R*128*(Dl+1) floats plus 16*W bytes, with R
+ *                    row blocks per band and W <= 256/R windows bounded from
+ *                    B, N, H and max_prefix_len (at most 134.5 MB for Dl 512;
+ *                    8.4 MB for one 16-node, 8-head request of 4096 tokens)
+ * Outputs (o, lse, workspace) must not overlap the inputs, including the first
+ * max_prefix_len rows at ckv and krope (checked; the host knows no more of the
+ * cache's extent).
  * bf16 inputs on the MFMA kernel need 16-byte aligned base pointers and row
  * strides that are multiples of 8 elements (INVALID_ARG otherwise) and at most
  * 2^24 elements (UNSUPPORTED otherwise); on the generic kernel, 2-byte aligned

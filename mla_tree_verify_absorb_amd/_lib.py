@@ -35,6 +35,7 @@ _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
     "ddtree_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ddtree_build_digest": (ctypes.c_char_p, []),
     "ddtree_build_mask": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "ddtree_verify_attn_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I64, _I32]),
     "ddtree_verify_attn_auto_splits": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I64]),
@@ -52,17 +53,36 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def built_digest(path: str = _LIB_PATH) -> str:
+    """The source digest stamped into a built library (loads it under a private handle)."""
+    fn = ctypes.CDLL(path).ddtree_build_digest
+    fn.restype = ctypes.c_char_p
+    return fn().decode()
+
+
+def is_current(path: str = _LIB_PATH) -> bool:
+    """True when the library exists and was built from the sources beside it."""
+    from .build import source_digest
+    return os.path.exists(path) and built_digest(path) == source_digest()
+
+
 def lib() -> ctypes.CDLL:
-    """Load the in-tree library (raises if it has not been built)."""
+    """Load the in-tree library.  Raises if it is not built, or if it was built from sources other than
+    the ones beside it (a stale build)."""
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m mla_tree_verify_absorb_amd.build`")
+        from .build import source_digest
         handle = ctypes.CDLL(_LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        got, want = handle.ddtree_build_digest().decode(), source_digest()
+        if got != want:
+            raise RuntimeError(f"{_LIB_PATH} was built from other sources (library digest {got}, sources {want}); "
+                               f"rebuild with `python -m mla_tree_verify_absorb_amd.build`")
         _lib = handle
     return _lib
 

@@ -99,11 +99,24 @@ int resolve_splits(bool mfma, int B, int N, int H, int64_t max_prefix_len, int n
   return num_splits > 0 ? num_splits : auto_schedule(mfma, B, N, H, max_prefix_len);
 }
 
-size_t workspace_bytes_for(bool mfma, int B, int N, int H, int Dl, int splits) {
+// Band schedule workspace, sized from the call: a workgroup (window, slot) keeps
+// at most two partials (the band cut at its window's start and the one cut at
+// its end), so windows * R * 2 partial slots of kRowsPerBlock rows (o then lse),
+// then one 16-byte record per window (record 0: the column total and window
+// count, record e: edge e's cut descriptor).
+int band_part_slots(int N, int H, int windows) {
+  const int64_t n_rb = ceil_div((int64_t)N * H, kRowsPerBlock);
+  const int64_t rbb = n_rb % kBandRowBlocks == 0 ? kBandRowBlocks : n_rb;
+  return (int)(2 * windows * rbb);
+}
+
+size_t workspace_bytes_for(bool mfma, int B, int N, int H, int Dl, int splits, int64_t max_prefix_len) {
   if (!mfma) return 0;
-  if (splits == 0)
-    return (size_t)kBandPartSlots * kRowsPerBlock * (uint64_t)(Dl + 1) * sizeof(float) +
-           kBandMaxWindows * 4 * sizeof(int);
+  if (splits == 0) {
+    const int windows = band_windows_bound(B, N, H, max_prefix_len);
+    return (size_t)band_part_slots(N, H, windows) * kRowsPerBlock * (uint64_t)(Dl + 1) * sizeof(float) +
+           (size_t)windows * 4 * sizeof(int);
+  }
   if (splits == 1) return 0;
   const uint64_t rows = (uint64_t)B * N * H;
   return (size_t)(splits * rows * (uint64_t)(Dl + 1) * sizeof(float));
@@ -111,7 +124,13 @@ size_t workspace_bytes_for(bool mfma, int B, int N, int H, int Dl, int splits) {
 
 }  // namespace
 
+#ifndef DDTREE_SOURCE_DIGEST
+#define DDTREE_SOURCE_DIGEST "unknown"
+#endif
+
 extern "C" {
+
+const char* ddtree_build_digest(void) { return DDTREE_SOURCE_DIGEST; }
 
 const char* ddtree_status_string(int status) {
   switch (status) {
@@ -152,7 +171,7 @@ size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, in
   if (B <= 0 || N <= 0 || H <= 0 || Dl <= 0 || num_splits < 0) return 0;
   const bool mfma = mfma_path(dtype, Dl, Dr);
   const int s = resolve_splits(mfma, B, N, H, max_prefix_len, num_splits);
-  return workspace_bytes_for(mfma, B, N, H, Dl, s);
+  return workspace_bytes_for(mfma, B, N, H, Dl, s, max_prefix_len);
 }
 
 int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr, const void* q_lat,
@@ -197,7 +216,7 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   // ---- workspace ----
   const int splits = resolve_splits(mfma, B, N, H, max_prefix_len, num_splits);
   if (splits > 1024) return DDTREE_ERR_UNSUPPORTED;
-  const size_t need = workspace_bytes_for(mfma, B, N, H, Dl, splits);
+  const size_t need = workspace_bytes_for(mfma, B, N, H, Dl, splits, max_prefix_len);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DDTREE_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return DDTREE_ERR_INVALID_ARG;
   // ---- aliasing (extents known on the host) ----
@@ -205,14 +224,19 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   const uint64_t es = dtype == DDTREE_BF16 ? 2 : 4;
   const uint64_t W = (uint64_t)(N + 31) / 32;
   const uint64_t tree_rows = (uint64_t)B * N;
+  // The prefix cache's true extent (offsets[B] rows) lives on the device; the
+  // host checks the first max_prefix_len rows at ckv and krope.
+  const uint64_t mp = (uint64_t)max_prefix_len;
   const Range ins[] = {range_of(q_lat, rows * Dl * es),
                        range_of(q_rope, Dr ? rows * Dr * es : 0),
                        range_of(prefix_offsets, (B + 1) * 8ull),
                        range_of(mask, tree_rows * W * 4),
                        range_of(ckv_tree, ((tree_rows - 1) * ld_ckv_tree + Dl) * es),
-                       range_of(krope_tree, Dr ? ((tree_rows - 1) * ld_krope_tree + Dr) * es : 0)};
+                       range_of(krope_tree, Dr ? ((tree_rows - 1) * ld_krope_tree + Dr) * es : 0),
+                       range_of(ckv, mp ? ((mp - 1) * (uint64_t)ld_ckv + Dl) * es : 0),
+                       range_of(krope, mp && Dr ? ((mp - 1) * (uint64_t)ld_krope + Dr) * es : 0)};
   const Range outs[] = {range_of(o, rows * Dl * 4), range_of(lse, rows * 4), range_of(workspace, need)};
-  if (any_overlap(outs, 3, ins, 6)) return DDTREE_ERR_INVALID_ARG;
+  if (any_overlap(outs, 3, ins, 8)) return DDTREE_ERR_INVALID_ARG;
 
   AttnArgs a;
   a.B = B;
@@ -245,10 +269,11 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = a.part_o + (uint64_t)splits * rows * Dl;
   } else if (splits == 0) {
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = a.part_o + (uint64_t)kBandPartSlots * kRowsPerBlock * Dl;
-    a.band_edges = reinterpret_cast<int*>(a.part_lse + (uint64_t)kBandPartSlots * kRowsPerBlock);
     a.band_windows = band_windows_bound(B, N, H, max_prefix_len);
+    const uint64_t slots = (uint64_t)band_part_slots(N, H, a.band_windows);
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + slots * kRowsPerBlock * Dl;
+    a.band_edges = reinterpret_cast<int*>(a.part_lse + slots * kRowsPerBlock);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;

@@ -36,10 +36,11 @@ struct AttnArgs {
   float* o;
   float* lse;
   // uniform schedule, splits > 1: part_o [splits][B*N*H][Dl], part_lse [splits][B*N*H]
-  // band schedule: part_o [kBandPartSlots][kRowsPerBlock][Dl], part_lse [kBandPartSlots][kRowsPerBlock]
+  // band schedule: part_o [slots][kRowsPerBlock][Dl], part_lse [slots][kRowsPerBlock] with
+  // slots = 2 * band_windows * (row blocks per band)
   float* part_o;
   float* part_lse;
-  int* band_edges;     // band schedule: [kBandMaxWindows][4] (after part_lse): [0] the total column
+  int* band_edges;     // band schedule: [band_windows][4] (after part_lse): [0] the total column
                        // count (int64) and the window count, [e] edge e's cut descriptor
   int band_windows;    // band schedule: most windows (host bound from the longest prefix; the
                        // kernel uses fewer when the columns run short)
@@ -58,9 +59,7 @@ constexpr int kKeysPerTile = 32;     // latent KV rows per LDS tile
 constexpr int kBandRowBlocks = 32;
 constexpr int kBandXcds = 8;
 constexpr int kBandWorkgroups = kBandXcds * kBandRowBlocks;   // 256, one per CU
-constexpr int kBandMaxWindows = kBandWorkgroups;               // R = 1
 constexpr int kBandMinWindowColumns = 8;   // fewest KV tile columns in a window
-constexpr int kBandPartSlots = 2 * kBandWorkgroups;
 constexpr int64_t kMaxBf16RowStride = int64_t(1) << 24;   // elements; keeps tile row offsets in 32 bits
 
 // KV-cache compaction (byte addressing; strides in bytes)

@@ -453,7 +453,9 @@ __device__ PieceCursor band_cursor_start(const AttnArgs& a, int n_rb, int block)
   // {cut here first, request, band, last window the band reaches}.  The band
   // holding column X_x is cut first at x when it starts inside window x - 1
   // (at or after X_{x-1}, before X_x).  Window 0's slot 0 stores {C, windows}.
-  if (c.slot == 0 && threadIdx.x == 0) {
+  // The workspace holds records for the host's window bound only (the combine
+  // kernel reads edges below the window count, which never exceeds it).
+  if (c.slot == 0 && threadIdx.x == 0 && c.win < a.band_windows) {
     if (c.win == 0) {
       reinterpret_cast<int4*>(a.band_edges)[0] =
           make_int4((int)(uint32_t)(uint64_t)C, (int)(uint32_t)((uint64_t)C >> 32), windows, 0);

@@ -14,9 +14,10 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session", autouse=True)
 def _built_library():
-    """Tests load the in-tree library; build it once only if nothing is built yet."""
+    """Tests load the in-tree library: build it if it is missing or was built from other sources (the
+    library carries a digest of its sources; the binding refuses a mismatch)."""
     from mla_tree_verify_absorb_amd import _lib
-    if not os.path.exists(_lib.library_path()):
+    if not _lib.is_current():
         from mla_tree_verify_absorb_amd.build import build
         build()
     yield

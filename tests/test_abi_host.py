@@ -38,6 +38,19 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(_lib._SIGNATURES)
 
 
+def test_rates_library_exports_its_header():
+    """The achievable-rate probes (bench context, not the verify path) live in their own library."""
+    from mla_tree_verify_absorb_amd import rates
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ddtree_rates.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(ddtree_rates_\w+)\s*\(", text)))
+    assert names and set(names) == set(rates.SIGNATURES)
+    lib = rates.lib()
+    assert all(hasattr(lib, n) for n in names)
+    assert lib.ddtree_rates_mfma_loop_flops(512, 10) == 512 * 4 * 10 * 4 * 32768
+    assert lib.ddtree_rates_mfma_loop(0, 10, A, None) == -1                 # rejected on the host
+    assert lib.ddtree_rates_stream_read(A, 100, 8, A, None) == -1           # not a multiple of 16
+
+
 def test_status_strings():
     assert dd.ddtree_status_string(OK) == "DDTREE_OK"
     assert dd.ddtree_status_string(INVALID) == "DDTREE_ERR_INVALID_ARG"
@@ -112,6 +125,11 @@ def test_verify_attn_rejects_aliasing():
     assert attn(o=A + 64) == INVALID                  # o overlaps q_lat
     assert attn(lse=A + (6 << 24) + 4096) == INVALID  # lse overlaps o
     assert attn(o=A + (5 << 24)) == INVALID           # o overlaps mask
+    # the first max_prefix_len (64) rows of the prefix cache: ckv rows end 73600 bytes past ckv, the
+    # rotary rows (1024 bytes in, 128 bytes each) 73728
+    assert attn(o=A + (2 << 24) + 4096) == INVALID            # o inside the latent rows
+    assert attn(lse=A + (2 << 24) + 73650) == INVALID         # lse inside the last rotary row only
+    assert attn(splits=4, ws=A + (2 << 24) + 32, ws_bytes=4 * 8 * 64 * 513 * 4) == INVALID   # workspace
 
 
 def test_workspace_contract():
@@ -126,8 +144,13 @@ def test_workspace_contract():
     assert attn(splits=-1) == INVALID
 
 
-# (window, slot, head/tail) partial slots of 128 rows x (Dl + 1) floats, then 8 edge descriptors of 4 ints
-BAND_WS = 2 * 8 * 32 * 128 * 513 * 4 + 256 * 16
+def band_ws(R, W, Dl=512):
+    """Band workspace for R row blocks per band and a bound of W windows: (window, slot, head/tail) partial
+    slots of 128 rows x (Dl + 1) floats, then W records of 4 ints."""
+    return 2 * W * R * 128 * (Dl + 1) * 4 + 16 * W
+
+
+BAND_WS = band_ws(32, 8)      # 32 row blocks per band, 8 windows: 134.5 MB
 
 
 def test_auto_schedule():
@@ -144,7 +167,8 @@ def test_auto_schedule():
     assert lib.ddtree_verify_attn_auto_splits(BF16, 4, 128, 8, 512, 64, 131072) == 0     # 8 row blocks
     assert lib.ddtree_verify_attn_auto_splits(BF16, 2, 1, 8, 512, 64, 100) == 0          # one partial row block
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 16, 16, 512, 64, 4096) == 0       # 2 row blocks
-    assert lib.ddtree_verify_attn_workspace_size(BF16, 2, 1, 8, 512, 64, 100, 0) == BAND_WS
+    # one row block per band: 2 requests x 5 columns, under 8 columns a window: one window
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 2, 1, 8, 512, 64, 100, 0) == band_ws(1, 1)
     # otherwise uniform splits: enough workgroups to cover 256 CUs, at least 4 tiles per split
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 24, 64, 512, 64, 4096) == 22      # 12 row blocks: 256 / 12
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 40, 64, 512, 64, 4096) == 13      # 20 row blocks
@@ -163,7 +187,23 @@ def test_auto_schedule():
     assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 8) == 8 * 64 * 64 * 513 * 4
     # the band schedule needs its workspace like any split
     assert attn(N=64, splits=0) == WORKSPACE
-    assert attn(N=64, splits=0, ws=A + (8 << 24), ws_bytes=BAND_WS - 4) == WORKSPACE
+    assert attn(N=64, splits=0, ws=A + (8 << 24), ws_bytes=band_ws(32, 1) - 4) == WORKSPACE   # max_len 64: 1 window
+
+
+def test_band_workspace_is_sized_from_the_call():
+    lib = dd.lib()
+    ws = lambda B, N, H, L: lib.ddtree_verify_attn_workspace_size(BF16, B, N, H, 512, 64, L, 0)
+    # the K2 workloads: 32 row blocks per band, 8 windows (the most for R = 32)
+    assert ws(1, 64, 64, 4096) == ws(16, 64, 64, 32768) == ws(4, 128, 64, 131072) == band_ws(32, 8)
+    # small requests: 130 columns / 8 = 16 windows (R = 1 or 4), far below the K2 size
+    assert ws(1, 16, 8, 4096) == band_ws(1, 16) == 8405248
+    assert ws(1, 64, 8, 4096) == band_ws(4, 16)
+    # the bound follows max_prefix_len: a 64-node, 64-head request with no prefix has 2 columns, one window
+    assert ws(1, 64, 64, 0) == band_ws(32, 1)
+    assert ws(1, 64, 64, 250) == band_ws(32, 1)        # 8 + 2 columns
+    assert ws(1, 64, 64, 800) == band_ws(32, 3)        # 25 + 2 columns
+    # a workspace of the size returned is accepted by the host checks (and one byte less is not)
+    assert attn(N=64, splits=0, max_len=800, ws=A + (8 << 24), ws_bytes=band_ws(32, 3) - 1) == WORKSPACE
 
 
 # ---------------------------------------------------------------- greedy_accept

@@ -33,6 +33,11 @@ def test_bench_json_contract():
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
     assert 0 < roof["frac"] < 1 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert "traffic" in roof   # counters belong to the long-context workload: null here
+    assert 0 < roof["frac_of_measured_mfma_loop"]
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0 and cpu["sample"]
-    assert d["reference_rates"]["gemm_bf16_tflops"] > 0 and d["reference_rates"]["copy_gbps"] > 0
+    assert cpu["host_cpus"] >= 1 and cpu["blas_threads"] == cpu["cores"] and "cpu_model" in cpu
+    ref = d["reference_rates"]
+    assert ref["gemm_bf16_tflops"] > 0 and ref["copy_gbps"] > 0
+    # the box's own ceilings: a back-to-back MFMA loop and a read-only stream, below the vendor peaks
+    assert 0 < ref["mfma_loop_bf16_tflops"] <= 2600 and 0 < ref["stream_read_gbps"] <= 8500
