@@ -14,7 +14,8 @@
  * Conventions shared by every entry point
  *   - Pointers marked "device" are HIP device memory owned by the caller; the
  *     library allocates nothing, keeps no state between calls and is safe to
- *     call from several host threads.
+ *     call from several host threads (the one exception is the per-GPU scratch
+ *     of ddtree_verify_attn_noalloc, described there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and returns; nothing synchronises.
  *   - Arrays are dense row-major (C order) unless a leading dimension (ld_*,
@@ -167,6 +168,37 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
                        const void* ckv_tree, int64_t ld_ckv_tree, const void* krope_tree, int64_t ld_krope_tree,
                        const uint32_t* mask, float softmax_scale, int32_t num_splits,
                        float* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ddtree_verify_attn_noalloc -- ddtree_verify_attn that allocates nothing and
+ * takes no workspace.
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, results and errors are those of ddtree_verify_attn
+ * (same kernels), without workspace / workspace_bytes.  The split partials live
+ * in one device array inside the library, DDTREE_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * per GPU, held by every GPU the library runs on until the process ends (its
+ * address is looked up once per device on the first call there).
+ *   - A call whose ddtree_verify_attn_workspace_size(...) exceeds the scratch
+ *     returns DDTREE_ERR_WORKSPACE and enqueues nothing (use ddtree_verify_attn
+ *     with a workspace then); K2 shapes with 32 row blocks per band and several
+ *     windows (e.g. 64 nodes x 64 heads over 4096 tokens) need 134.5 MB.
+ *   - Every call on a GPU shares that GPU's scratch, which keeps the last
+ *     call's contents; nothing in it needs clearing (each call writes every
+ *     byte it reads).  Calls that overlap on one GPU (on different streams, or
+ *     from several host threads without ordering) race on it.
+ *   - DDTREE_ERR_HIP also reports a failed lookup of the scratch's address.
+ */
+#define DDTREE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+int ddtree_verify_attn_noalloc(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
+                               const void* q_lat, const void* q_rope,
+                               const void* ckv, int64_t ld_ckv, const void* krope, int64_t ld_krope,
+                               const int64_t* prefix_offsets, int64_t max_prefix_len,
+                               const void* ckv_tree, int64_t ld_ckv_tree, const void* krope_tree,
+                               int64_t ld_krope_tree, const uint32_t* mask, float softmax_scale, int32_t num_splits,
+                               float* o, float* lse, void* stream);
 
 /*
  * ddtree_greedy_accept -- target argmax per node and the accepted path.

@@ -26,6 +26,7 @@ DDTREE_BF16 = 1
 DDTREE_MAX_NODES = 256
 DDTREE_MAX_DEPTH = 64
 DDTREE_MAX_PROPOSALS = 64
+DDTREE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -41,6 +42,8 @@ _SIGNATURES = {
     "ddtree_verify_attn_auto_splits": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I64]),
     "ddtree_verify_attn": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _I64, _P, _I64,
                                           _P, _I64, _P, _I64, _P, _F32, _I32, _P, _P, _P, _SZ, _P]),
+    "ddtree_verify_attn_noalloc": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _I64, _P,
+                                                  _I64, _P, _I64, _P, _I64, _P, _F32, _I32, _P, _P, _P]),
     "ddtree_greedy_accept": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "ddtree_compact_kv": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P,
                                          _I64, _P]),
@@ -208,6 +211,31 @@ def ddtree_verify_attn(q_lat: torch.Tensor, q_rope: torch.Tensor, ckv: torch.Ten
                                   _ptr(krope_tree), ld_krope_t, _ptr(mask), float(softmax_scale), int(num_splits),
                                   _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev, stream))
     _check(st, "ddtree_verify_attn")
+    return o, lse
+
+
+def ddtree_verify_attn_noalloc(q_lat: torch.Tensor, q_rope: torch.Tensor, ckv: torch.Tensor, krope: torch.Tensor,
+                               prefix_offsets: torch.Tensor, max_prefix_len: int, ckv_tree: torch.Tensor,
+                               krope_tree: torch.Tensor, mask: torch.Tensor, softmax_scale: float, *,
+                               o: torch.Tensor, lse: torch.Tensor, num_splits: int = 0, stream=None):
+    """ddtree_verify_attn without a workspace: the library's own per-GPU scratch holds the split partials.
+    o and lse are the caller's (nothing is allocated here either)."""
+    B, N, H, Dl = q_lat.shape
+    Dr = q_rope.shape[-1]
+    assert q_lat.is_contiguous() and q_rope.is_contiguous() and tuple(q_rope.shape[:3]) == (B, N, H)
+    code = _dtype_code(q_lat)
+    for t in (q_rope, ckv, krope, ckv_tree, krope_tree):
+        assert t.dtype == q_lat.dtype, "all latent inputs must share one dtype"
+    assert o.dtype == torch.float32 and o.is_contiguous() and tuple(o.shape) == (B, N, H, Dl)
+    assert lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, N, H)
+    st = lib().ddtree_verify_attn_noalloc(code, B, N, H, Dl, Dr, _ptr(q_lat), _ptr(q_rope), _ptr(ckv),
+                                          _rows_ld(ckv, Dl, "ckv"), _ptr(krope), _rows_ld(krope, Dr, "krope"),
+                                          _ptr(prefix_offsets), int(max_prefix_len), _ptr(ckv_tree),
+                                          _tree_ld(ckv_tree, B, N, Dl, "ckv_tree"), _ptr(krope_tree),
+                                          _tree_ld(krope_tree, B, N, Dr, "krope_tree"), _ptr(mask),
+                                          float(softmax_scale), int(num_splits), _ptr(o), _ptr(lse),
+                                          _stream(q_lat.device, stream))
+    _check(st, "ddtree_verify_attn_noalloc")
     return o, lse
 
 

@@ -3,6 +3,7 @@
 // call enqueues nothing (and can be tested on a machine without a GPU).
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/ddtree.h"
 #include "ddtree_internal.h"
@@ -120,6 +121,43 @@ size_t workspace_bytes_for(bool mfma, int B, int N, int H, int Dl, int splits, i
   if (splits == 1) return 0;
   const uint64_t rows = (uint64_t)B * N * H;
   return (size_t)(splits * rows * (uint64_t)(Dl + 1) * sizeof(float));
+}
+
+// ---- scratch of ddtree_verify_attn_noalloc ----
+// One file-scope device array; each GPU the library runs on holds its own copy
+// for the life of the process.  In host code `scratch` is only a stand-in
+// symbol: its device address on a GPU comes from hipGetSymbolAddress, called
+// once per device with that device current, and only that address is ever
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[DDTREE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream`.
+hipError_t scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -285,6 +323,24 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
     e = launch_verify_attn_generic(a, dtype == DDTREE_BF16, s);
   }
   return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP;
+}
+
+int ddtree_verify_attn_noalloc(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
+                               const void* q_lat, const void* q_rope, const void* ckv, int64_t ld_ckv,
+                               const void* krope, int64_t ld_krope, const int64_t* prefix_offsets,
+                               int64_t max_prefix_len, const void* ckv_tree, int64_t ld_ckv_tree,
+                               const void* krope_tree, int64_t ld_krope_tree, const uint32_t* mask,
+                               float softmax_scale, int32_t num_splits, float* o, float* lse, void* stream) {
+  // the size check comes first: a call too large for the scratch touches no device state
+  const size_t need = ddtree_verify_attn_workspace_size(dtype, B, N, H, Dl, Dr, max_prefix_len, num_splits);
+  if (need > DDTREE_NOALLOC_SCRATCH_BYTES) return DDTREE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && B > 0) {
+    if (scratch_for_stream(static_cast<hipStream_t>(stream), &ws) != hipSuccess) return DDTREE_ERR_HIP;
+  }
+  return ddtree_verify_attn(dtype, B, N, H, Dl, Dr, q_lat, q_rope, ckv, ld_ckv, krope, ld_krope, prefix_offsets,
+                            max_prefix_len, ckv_tree, ld_ckv_tree, krope_tree, ld_krope_tree, mask, softmax_scale,
+                            num_splits, o, lse, ws, ws ? (size_t)DDTREE_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int ddtree_greedy_accept(const float* logits, int64_t ld_logits, const int32_t* tokens, const int32_t* parents,

@@ -206,6 +206,31 @@ def test_band_workspace_is_sized_from_the_call():
     assert attn(N=64, splits=0, max_len=800, ws=A + (8 << 24), ws_bytes=band_ws(32, 3) - 1) == WORKSPACE
 
 
+def attn_noalloc(**kw):
+    """The no-allocation variant with attn()'s fake pointers (no workspace arguments)."""
+    a = dict(dtype=BF16, B=1, N=8, H=64, Dl=512, Dr=64, q=A, qr=A + (1 << 24), ckv=A + (2 << 24), ld_ckv=576,
+             krope=A + (2 << 24) + 1024, ld_krope=576, offs=A + (3 << 24), max_len=64, ckv_t=A + (4 << 24),
+             ld_ckv_t=576, krope_t=A + (4 << 24) + 1024, ld_krope_t=576, mask=A + (5 << 24), scale=0.07,
+             splits=1, o=A + (6 << 24), lse=A + (7 << 24))
+    a.update(kw)
+    return dd.lib().ddtree_verify_attn_noalloc(*a.values(), None)
+
+
+def test_noalloc_rejects_what_its_scratch_cannot_hold():
+    """Checked before anything touches the device: a shape whose workspace exceeds the 64 MiB scratch is
+    refused with DDTREE_ERR_WORKSPACE, and invalid arguments keep ddtree_verify_attn's errors."""
+    lib = dd.lib()
+    assert dd.DDTREE_NOALLOC_SCRATCH_BYTES == 64 << 20
+    big = lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 0)
+    assert big > dd.DDTREE_NOALLOC_SCRATCH_BYTES
+    assert attn_noalloc(N=64, splits=0, max_len=4096) == WORKSPACE         # 64 nodes x 64 heads, 4096 tokens
+    assert attn_noalloc(N=64, splits=16, max_len=4096) == WORKSPACE        # 16 uniform splits of 4096 rows
+    assert attn_noalloc(B=0) == OK
+    assert attn_noalloc(N=0) == INVALID
+    assert attn_noalloc(q=None) == INVALID                                 # splits=1: no scratch needed
+    assert attn_noalloc(o=A + 64) == INVALID
+
+
 # ---------------------------------------------------------------- greedy_accept
 
 def acc(logits=A, ld=512, tokens=A + (1 << 24), parents=A + (1 << 24) + 4096, B=1, N=8, V=512,
