@@ -426,18 +426,35 @@ __device__ __forceinline__ PieceCursor uniform_cursor(const PieceCursor& v) {
   return c;
 }
 
+// Windows this short (in tile columns) with 32 row blocks per band take the
+// slot-major mapping below: a window's KV (36 KB a column) is then smaller than
+// the queries of an XCD's 32 row blocks (4.7 MB), which all start at once.
+constexpr int kSlotMajorMaxColumns = 4 * kBandRowBlocks;
+
 __device__ PieceCursor band_cursor_start(const AttnArgs& a, int n_rb, int block) {
   PieceCursor c;
   c.rbb = band_row_blocks(n_rb);
-  const int idx = block / kBandXcds;                    // workgroup i runs on XCD i % 8
-  c.slot = idx % c.rbb;
-  c.win = (idx / c.rbb) * kBandXcds + block % kBandXcds;
   c.nb = n_rb / c.rbb;
   c.ntt = (a.N + KT - 1) / KT;
   const int64_t C = uniform64(band_columns_total(a.prefix_offsets, a.B, c.nb, c.ntt));
   // at least kBandMinWindowColumns columns a window (bounds the pieces per band,
   // and so the partial traffic, and keeps every window non-empty)
   const int windows = (int)min<int64_t>(a.band_windows, max<int64_t>(1, C / kBandMinWindowColumns));
+  // Workgroup i runs on XCD i % 8.  Window-major (the default): the R workgroups
+  // of window x run on XCD x % 8, so each KV tile is fetched once per L2 and each
+  // XCD loads the queries of all R row blocks.  Slot-major (R = 32, short
+  // windows): XCD x runs row blocks 4x .. 4x + 3 of every window, so each row
+  // block's queries are fetched once per L2 and the short windows' KV streams to
+  // all 8 XCDs instead.  Both are bijections of the 256 workgroups.
+  const int idx = block / kBandXcds, xcd = block % kBandXcds;
+  if (c.rbb == kBandRowBlocks && C <= (int64_t)windows * kSlotMajorMaxColumns) {
+    constexpr int per_xcd = kBandRowBlocks / kBandXcds;   // 4
+    c.slot = xcd * per_xcd + idx % per_xcd;
+    c.win = idx / per_xcd;
+  } else {
+    c.slot = idx % c.rbb;
+    c.win = (idx / c.rbb) * kBandXcds + xcd;
+  }
   c.X0 = c.win < windows ? window_edge(C, c.win, windows) : C;
   c.X1 = c.win < windows ? window_edge(C, c.win + 1, windows) : C;
   int64_t S;

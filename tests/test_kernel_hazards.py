@@ -9,6 +9,11 @@ of a VGPR and an MFMA that reads it (the ISA asks for 2 wait states here).  The 
 the asm itself provides (after the last S^T MFMA, before the first O^T MFMA, after the tile
 loop) are written into the asm statements and need no check.
 
+The O^T accumulators stay in AGPRs across the whole tile loop: the third test requires that the
+compiler moves no accumulator through VGPRs (v_accvgpr_read / v_accvgpr_write) between the first
+and the last MFMA of the kernel, since an AGPR written that way just before an asm MFMA that
+accumulates into it would need wait states the compiler does not know to insert.
+
 The tile copies (direct-to-LDS loads) also live in inline asm, each writing M0 right before
 its load.  The second test requires that nothing else in the kernel reads or writes M0, so
 that a compiler-generated M0 value can never be live across one of those statements.
@@ -74,11 +79,20 @@ def test_m0_is_written_only_by_the_tile_copies(tmp_path_factory):
     uses = [(i, l) for i, l in enumerate(lines) if re.search(r"\bm0\b", l)]
     assert uses, "kernel not found in the assembly"
     for i, line in uses:
-        # s_mov_b32 m0, <sgpr>; v_xad_u32 / v_add_u32 (the lane address); global_load_lds_dwordx4
-        assert re.match(r"s_mov_b32 m0, s\d+$", line), line
+        # s_mov_b32 m0, <scalar register>; v_xad_u32 / v_add_u32 (the lane address); global_load_lds_dwordx4
+        assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi|ttmp\d+)$", line), line
         assert lines[i + 1].startswith(("v_xad_u32", "v_add_u32")), lines[i + 1]
         assert lines[i + 2].startswith("global_load_lds_dwordx4"), lines[i + 2]
     assert len(uses) == sum(l.startswith("global_load_lds_dwordx4") for l in lines)
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_no_accumulator_moves_inside_the_mfma_region(tmp_path_factory):
+    lines = _kernel_asm(tmp_path_factory)
+    mf = [i for i, l in enumerate(lines) if l.startswith("v_mfma")]
+    assert len(mf) >= 68, "kernel not found in the assembly"
+    moves = [l for l in lines[mf[0]:mf[-1]] if l.startswith(("v_accvgpr_read", "v_accvgpr_write", "v_accvgpr_mov"))]
+    assert not moves, f"{len(moves)} accumulator moves between MFMAs, e.g. {moves[:3]}"
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
