@@ -383,6 +383,33 @@ def test_attn_bf16_small_bands_random_shapes(seed):
     print(f"seed {seed}: B={B} N={N} H={H}: normwise o err {eo:.2e}, lse err {el:.2e}")
 
 
+@pytest.mark.parametrize("case", [
+    dict(B=1, N=64, prefix=("list", [100])),                      # one window
+    dict(B=3, N=64, prefix=("list", [300, 1000, 50])),            # 6 windows, cuts across band boundaries
+    dict(B=2, N=128, prefix=("list", [2000, 700])),               # two bands per request, 8 windows
+    dict(B=5, N=64, prefix=("list", [0, 33, 400, 4000, 9])),      # empty and short prefixes
+])
+def test_attn_bf16_slot_major_short_windows(case):
+    """Bands of 32 row blocks (64 heads) cut into windows of at most 128 tile columns take the slot-major
+    mapping (each XCD runs 4 row blocks of every window); sampled nodes of every request against the oracle,
+    and a repeat call is bitwise equal."""
+    params = dict(K2)
+    params.update(H=64, tree=("bounded", 8, 4), **case)
+    w = make_workload(seed=71 + case["B"], **params)
+    dw = DevWorkload(w)
+    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, w.B, w.N, w.H, w.Dl, w.Dr, dw.max_len) == 0
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    torch.cuda.synchronize()
+    nodes = [(b, i) for b in range(w.B) for i in sorted({0, 1, w.N // 2, w.N - 1})]
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    o2, lse2 = dw.attn(mask)                                       # repeat calls are bitwise equal
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    print(f"slot-major {case}: normwise o err {eo:.2e}, lse err {el:.2e}")
+
+
 @pytest.mark.parametrize("H,max_len", [(8, 0), (8, 100), (64, 0)])
 def test_attn_bf16_band_understated_max_prefix_len(H, max_len):
     """The band schedule's window count is bounded on the host from max_prefix_len and on the
