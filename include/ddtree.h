@@ -26,7 +26,11 @@
  *     depend on device data (a malformed tree) are reported on the device
  *     through tree_ok.
  *   - Outputs must not overlap inputs or each other (checked where the
- *     extents are known on the host).
+ *     extents are known on the host); a buffer whose extent runs past the top
+ *     of the address space is DDTREE_ERR_INVALID_ARG.
+ *   - Row strides (ld_*) and max_prefix_len above DDTREE_MAX_EXTENT are
+ *     DDTREE_ERR_UNSUPPORTED, so that every extent the host computes fits in
+ *     64 bits.
  *   - Tree layout: node 0 is the root (the last committed token), parent[0] =
  *     -1 and 0 <= parent[i] < i for i >= 1; at most DDTREE_MAX_NODES nodes.
  */
@@ -43,6 +47,7 @@ extern "C" {
 #define DDTREE_MAX_NODES 256
 #define DDTREE_MAX_DEPTH 64      /* draft depths offered to ddtree_build_tree */
 #define DDTREE_MAX_PROPOSALS 64  /* proposals per depth for ddtree_build_tree */
+#define DDTREE_MAX_EXTENT ((int64_t)1 << 40) /* largest row stride (elements) and prefix length (rows) */
 
 typedef enum {
   DDTREE_OK = 0,
@@ -151,7 +156,10 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  * bf16 inputs on the MFMA kernel need 16-byte aligned base pointers and row
  * strides that are multiples of 8 elements (INVALID_ARG otherwise) and at most
  * 2^24 elements (UNSUPPORTED otherwise); on the generic kernel, 2-byte aligned
- * pointers.  Requests whose tree_ok is 0 give undefined o/lse.
+ * pointers.  B*N*H above INT32_MAX/4 and num_splits above 1024 are UNSUPPORTED.
+ * Requests whose tree_ok is 0 give undefined o/lse.
+ * The two sizing queries take any arguments: for a shape the call would refuse
+ * they return 0 (workspace bytes) and 1 (split count).
  */
 size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                          int64_t max_prefix_len, int32_t num_splits);

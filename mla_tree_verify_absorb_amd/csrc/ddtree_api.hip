@@ -12,22 +12,50 @@ using namespace ddtree;
 
 namespace {
 
+// Byte extents are computed with overflow checks: kBadExtent stands for one that
+// does not fit in 64 bits, and a buffer whose extent is bad or runs past the top
+// of the address space is rejected like an overlap.
+constexpr uint64_t kBadExtent = UINT64_MAX;
+
+uint64_t mul_ext(uint64_t a, uint64_t b) {
+  uint64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? kBadExtent : r;
+}
+
+uint64_t add_ext(uint64_t a, uint64_t b) {
+  uint64_t r;
+  return __builtin_add_overflow(a, b, &r) ? kBadExtent : r;
+}
+
+// Bytes spanned by `rows` rows of `width` elements of `es` bytes, `ld` elements apart.
+uint64_t rows_bytes(uint64_t rows, uint64_t ld, uint64_t width, uint64_t es) {
+  if (rows == 0 || width == 0) return 0;
+  return mul_ext(add_ext(mul_ext(rows - 1, ld), width), es);
+}
+
 struct Range {
   uintptr_t lo, hi;   // [lo, hi)
+  bool bad;           // the extent does not fit the address space
 };
 
 Range range_of(const void* p, uint64_t bytes) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return Range{lo, lo + bytes};
+  uintptr_t hi;
+  const bool bad = bytes == kBadExtent || __builtin_add_overflow(lo, bytes, &hi);
+  return bad ? Range{lo, lo, true} : Range{lo, hi, false};
 }
 
 bool overlaps(Range a, Range b) {
+  if (a.bad || b.bad) return true;
   if (a.lo == a.hi || b.lo == b.hi) return false;
   return a.lo < b.hi && b.lo < a.hi;
 }
 
 bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_in; ++i)
+    if (ins[i].bad) return true;
   for (int i = 0; i < n_out; ++i) {
+    if (outs[i].bad) return true;
     for (int j = 0; j < n_in; ++j)
       if (overlaps(outs[i], ins[j])) return true;
     for (int j = i + 1; j < n_out; ++j)
@@ -83,10 +111,22 @@ bool band_schedule_applies(bool mfma, int N, int H) {
 int band_windows_bound(int B, int N, int H, int64_t max_prefix_len) {
   const int64_t n_rb = ceil_div((int64_t)N * H, kRowsPerBlock);
   const int64_t rbb = n_rb % kBandRowBlocks == 0 ? kBandRowBlocks : n_rb;
-  const int64_t cols = (int64_t)B * (n_rb / rbb) * (ceil_div(max_prefix_len, kKeysPerTile) + ceil_div(N, kKeysPerTile));
+  const int64_t per_band = ceil_div(max_prefix_len, kKeysPerTile) + ceil_div(N, kKeysPerTile);
+  int64_t cols;
+  if (__builtin_mul_overflow((int64_t)B * (n_rb / rbb), per_band, &cols)) cols = INT64_MAX;
   const int64_t w = cols / kBandMinWindowColumns;
   const int64_t most = kBandWorkgroups / rbb;
   return (int)(w < 1 ? 1 : (w > most ? most : w));
+}
+
+// Shapes the attention entry points take: B N H query rows within INT32_MAX / 4,
+// a prefix bound within DDTREE_MAX_EXTENT and at most kMaxSplits explicit splits.
+constexpr int kMaxSplits = 1024;
+
+bool attn_shape_supported(int B, int N, int H, int64_t max_prefix_len, int num_splits) {
+  int64_t rows;
+  if (__builtin_mul_overflow((int64_t)B * N, (int64_t)H, &rows)) return false;
+  return rows <= INT32_MAX / 4 && max_prefix_len <= DDTREE_MAX_EXTENT && num_splits <= kMaxSplits;
 }
 
 int auto_schedule(bool mfma, int B, int N, int H, int64_t max_prefix_len) {
@@ -189,7 +229,7 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
   if (!parents || !mask || !depth || !tree_ok) return DDTREE_ERR_INVALID_ARG;
   const uint64_t n = (uint64_t)B * N;
   const uint64_t W = (uint64_t)(N + 31) / 32;
-  const Range ins[] = {range_of(parents, n * 4), range_of(prefix_offsets, prefix_offsets ? (B + 1) * 8ull : 0)};
+  const Range ins[] = {range_of(parents, n * 4), range_of(prefix_offsets, prefix_offsets ? ((uint64_t)B + 1) * 8 : 0)};
   const Range outs[] = {range_of(mask, n * W * 4), range_of(depth, n * 4), range_of(positions, positions ? n * 8 : 0),
                         range_of(tree_ok, (uint64_t)B * 4)};
   if (any_overlap(outs, 4, ins, 2)) return DDTREE_ERR_INVALID_ARG;
@@ -200,13 +240,15 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
 
 int32_t ddtree_verify_attn_auto_splits(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                        int64_t max_prefix_len) {
-  if (B <= 0 || N <= 0 || H <= 0) return 1;
+  if (B <= 0 || N <= 0 || H <= 0 || max_prefix_len < 0 || !attn_shape_supported(B, N, H, max_prefix_len, 0))
+    return 1;
   return auto_schedule(mfma_path(dtype, Dl, Dr), B, N, H, max_prefix_len);
 }
 
 size_t ddtree_verify_attn_workspace_size(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                          int64_t max_prefix_len, int32_t num_splits) {
-  if (B <= 0 || N <= 0 || H <= 0 || Dl <= 0 || num_splits < 0) return 0;
+  if (B <= 0 || N <= 0 || H <= 0 || Dl <= 0 || num_splits < 0 || max_prefix_len < 0) return 0;
+  if (!attn_shape_supported(B, N, H, max_prefix_len, num_splits)) return 0;
   const bool mfma = mfma_path(dtype, Dl, Dr);
   const int s = resolve_splits(mfma, B, N, H, max_prefix_len, num_splits);
   return workspace_bytes_for(mfma, B, N, H, Dl, s, max_prefix_len);
@@ -227,7 +269,7 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   if (!mfma && (Dl > 512 || Dr > 512)) return DDTREE_ERR_UNSUPPORTED;
   if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
     return DDTREE_ERR_INVALID_ARG;
-  if ((int64_t)B * N * H > INT32_MAX / 4) return DDTREE_ERR_UNSUPPORTED;
+  if (!attn_shape_supported(B, N, H, max_prefix_len, num_splits)) return DDTREE_ERR_UNSUPPORTED;
   if (B == 0) return DDTREE_OK;
   // ---- pointers and strides ----
   if (!q_lat || !prefix_offsets || !ckv_tree || !mask || !o || !lse) return DDTREE_ERR_INVALID_ARG;
@@ -251,9 +293,11 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
         ld_krope_tree > kMaxBf16RowStride)
       return DDTREE_ERR_UNSUPPORTED;
   }
+  if (ld_ckv > DDTREE_MAX_EXTENT || ld_krope > DDTREE_MAX_EXTENT || ld_ckv_tree > DDTREE_MAX_EXTENT ||
+      ld_krope_tree > DDTREE_MAX_EXTENT)
+    return DDTREE_ERR_UNSUPPORTED;
   // ---- workspace ----
   const int splits = resolve_splits(mfma, B, N, H, max_prefix_len, num_splits);
-  if (splits > 1024) return DDTREE_ERR_UNSUPPORTED;
   const size_t need = workspace_bytes_for(mfma, B, N, H, Dl, splits, max_prefix_len);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DDTREE_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return DDTREE_ERR_INVALID_ARG;
@@ -267,12 +311,12 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   const uint64_t mp = (uint64_t)max_prefix_len;
   const Range ins[] = {range_of(q_lat, rows * Dl * es),
                        range_of(q_rope, Dr ? rows * Dr * es : 0),
-                       range_of(prefix_offsets, (B + 1) * 8ull),
+                       range_of(prefix_offsets, ((uint64_t)B + 1) * 8),
                        range_of(mask, tree_rows * W * 4),
-                       range_of(ckv_tree, ((tree_rows - 1) * ld_ckv_tree + Dl) * es),
-                       range_of(krope_tree, Dr ? ((tree_rows - 1) * ld_krope_tree + Dr) * es : 0),
-                       range_of(ckv, mp ? ((mp - 1) * (uint64_t)ld_ckv + Dl) * es : 0),
-                       range_of(krope, mp && Dr ? ((mp - 1) * (uint64_t)ld_krope + Dr) * es : 0)};
+                       range_of(ckv_tree, rows_bytes(tree_rows, ld_ckv_tree, Dl, es)),
+                       range_of(krope_tree, rows_bytes(tree_rows, ld_krope_tree, Dr, es)),
+                       range_of(ckv, rows_bytes(mp, ld_ckv, Dl, es)),
+                       range_of(krope, rows_bytes(mp, ld_krope, Dr, es))};
   const Range outs[] = {range_of(o, rows * Dl * 4), range_of(lse, rows * 4), range_of(workspace, need)};
   if (any_overlap(outs, 3, ins, 8)) return DDTREE_ERR_INVALID_ARG;
 
@@ -348,12 +392,12 @@ int ddtree_greedy_accept(const float* logits, int64_t ld_logits, const int32_t* 
                          int32_t* accept_nodes, int32_t* commit_tokens, void* stream) {
   if (B < 0 || N < 1 || V < 1 || ld_logits < V) return DDTREE_ERR_INVALID_ARG;
   if (N > DDTREE_MAX_NODES) return DDTREE_ERR_UNSUPPORTED;
-  if ((int64_t)B * N > INT32_MAX) return DDTREE_ERR_UNSUPPORTED;
+  if ((int64_t)B * N > INT32_MAX || ld_logits > DDTREE_MAX_EXTENT) return DDTREE_ERR_UNSUPPORTED;
   if (B == 0) return DDTREE_OK;
   if (!logits || !tokens || !parents || !target_argmax || !accept_len || !accept_nodes || !commit_tokens)
     return DDTREE_ERR_INVALID_ARG;
   const uint64_t n = (uint64_t)B * N;
-  const Range ins[] = {range_of(logits, ((n - 1) * (uint64_t)ld_logits + V) * 4), range_of(tokens, n * 4),
+  const Range ins[] = {range_of(logits, rows_bytes(n, ld_logits, V, 4)), range_of(tokens, n * 4),
                        range_of(parents, n * 4)};
   const Range outs[] = {range_of(target_argmax, n * 4), range_of(accept_len, (uint64_t)B * 4),
                         range_of(accept_nodes, n * 4), range_of(commit_tokens, n * 4)};
@@ -375,6 +419,9 @@ int ddtree_compact_kv(int32_t dtype, int32_t B, int32_t N, int32_t Dl, int32_t D
   if (Dr > 0 && (!krope_tree || !krope)) return DDTREE_ERR_INVALID_ARG;
   if (ld_ckv_tree < Dl || ld_ckv < Dl || (Dr > 0 && (ld_krope_tree < Dr || ld_krope < Dr)))
     return DDTREE_ERR_INVALID_ARG;
+  if (ld_ckv_tree > DDTREE_MAX_EXTENT || ld_ckv > DDTREE_MAX_EXTENT || ld_krope_tree > DDTREE_MAX_EXTENT ||
+      ld_krope > DDTREE_MAX_EXTENT)
+    return DDTREE_ERR_UNSUPPORTED;
   const int64_t es = dtype == DDTREE_BF16 ? 2 : 4;
   if (!aligned_to(ckv_tree, (unsigned)es) || !aligned_to(ckv, (unsigned)es) ||
       (Dr > 0 && (!aligned_to(krope_tree, (unsigned)es) || !aligned_to(krope, (unsigned)es))))
@@ -382,9 +429,11 @@ int ddtree_compact_kv(int32_t dtype, int32_t B, int32_t N, int32_t Dl, int32_t D
   const uint64_t n = (uint64_t)B * N;
   const Range ctrl[] = {range_of(accept_len, (uint64_t)B * 4), range_of(accept_nodes, n * 4),
                         range_of(dest_rows, (uint64_t)B * 8)};
-  const Range trees[] = {range_of(ckv_tree, ((n - 1) * ld_ckv_tree + Dl) * es),
-                         range_of(krope_tree, Dr ? ((n - 1) * ld_krope_tree + Dr) * es : 0)};
+  const Range trees[] = {range_of(ckv_tree, rows_bytes(n, ld_ckv_tree, Dl, es)),
+                         range_of(krope_tree, rows_bytes(n, ld_krope_tree, Dr, es))};
   // the tree rows (which may interleave, as views of one fused row) must not alias the path arrays
+  for (const Range& c : ctrl)
+    if (c.bad) return DDTREE_ERR_INVALID_ARG;
   for (const Range& t : trees)
     for (const Range& c : ctrl)
       if (overlaps(t, c)) return DDTREE_ERR_INVALID_ARG;
@@ -440,6 +489,10 @@ int ddtree_rope_tree(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dr,
   if (dtype != DDTREE_F32 && dtype != DDTREE_BF16) return DDTREE_ERR_UNSUPPORTED;
   if (B < 0 || N < 1 || H < 1 || Dr < 2 || (Dr & 1)) return DDTREE_ERR_INVALID_ARG;
   if (N > DDTREE_MAX_NODES || Dr > kMaxRopeDim) return DDTREE_ERR_UNSUPPORTED;
+  // the kernel indexes nodes and a node's (H + 1) rotary rows of Dr elements in 32 bits
+  if ((int64_t)B * N > INT32_MAX || ((int64_t)H + 1) * Dr > INT32_MAX ||
+      (krope_tree && ld_krope_tree > DDTREE_MAX_EXTENT))
+    return DDTREE_ERR_UNSUPPORTED;
   if (B == 0 || (!q_rope && !krope_tree)) return DDTREE_OK;
   if (!positions || !inv_freq) return DDTREE_ERR_INVALID_ARG;
   if (krope_tree && ld_krope_tree < Dr) return DDTREE_ERR_INVALID_ARG;
@@ -448,8 +501,8 @@ int ddtree_rope_tree(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dr,
     return DDTREE_ERR_INVALID_ARG;
   const uint64_t n = (uint64_t)B * N;
   const Range ins[] = {range_of(positions, n * 8), range_of(inv_freq, (uint64_t)(Dr / 2) * 8)};
-  const Range outs[] = {range_of(q_rope, q_rope ? n * H * Dr * es : 0),
-                        range_of(krope_tree, krope_tree ? ((n - 1) * ld_krope_tree + Dr) * es : 0)};
+  const Range outs[] = {range_of(q_rope, q_rope ? mul_ext(mul_ext(n, (uint64_t)H * Dr), es) : 0),
+                        range_of(krope_tree, krope_tree ? rows_bytes(n, ld_krope_tree, Dr, es) : 0)};
   if (any_overlap(outs, 2, ins, 2)) return DDTREE_ERR_INVALID_ARG;
   RopeArgs a{};
   a.B = B;
