@@ -145,11 +145,14 @@ int ddtree_build_mask(const int32_t* parents, int32_t B, int32_t N, const int64_
  *   workspace        device scratch of workspace_bytes >=
  *                    ddtree_verify_attn_workspace_size(...) with the same shape,
  *                    max_prefix_len and num_splits (may be NULL when that size
- *                    is 0); S splits take S*B*N*H*(Dl+1) floats, the band
- *                    schedule 2*W*R*128*(Dl+1) floats plus 16*W bytes, with R
- *                    row blocks per band and W <= 256/R windows bounded from
- *                    B, N, H and max_prefix_len (at most 134.5 MB for Dl 512;
- *                    8.4 MB for one 16-node, 8-head request of 4096 tokens)
+ *                    is 0).  It holds one record per row of a split or band
+ *                    piece: the row's output in fp16 under a power-of-two
+ *                    scale plus two floats, 2*Dl + 8 bytes.  S splits take
+ *                    S*B*N*H records, the band schedule 2*W*R*128 records plus
+ *                    16*W bytes, with R row blocks per band and W <= 256/R
+ *                    windows bounded from B, N, H and max_prefix_len (at most
+ *                    67.6 MB for Dl 512; 4.2 MB for one 16-node, 8-head
+ *                    request of 4096 tokens)
  * Outputs (o, lse, workspace) must not overlap the inputs, including the first
  * max_prefix_len rows at ckv and krope (checked; the host knows no more of the
  * cache's extent).
@@ -185,20 +188,21 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Arguments, results and errors are those of ddtree_verify_attn
  * (same kernels), without workspace / workspace_bytes.  The split partials live
- * in one device array inside the library, DDTREE_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * in one device array inside the library, DDTREE_NOALLOC_SCRATCH_BYTES (72 MiB)
  * per GPU, held by every GPU the library runs on until the process ends (its
  * address is looked up once per device on the first call there).
  *   - A call whose ddtree_verify_attn_workspace_size(...) exceeds the scratch
  *     returns DDTREE_ERR_WORKSPACE and enqueues nothing (use ddtree_verify_attn
- *     with a workspace then); K2 shapes with 32 row blocks per band and several
- *     windows (e.g. 64 nodes x 64 heads over 4096 tokens) need 134.5 MB.
+ *     with a workspace then).  The band schedule needs at most 67.6 MB, so
+ *     it always fits; explicit split counts above 17 at 64 nodes x 64 heads do
+ *     not.
  *   - Every call on a GPU shares that GPU's scratch, which keeps the last
  *     call's contents; nothing in it needs clearing (each call writes every
  *     byte it reads).  Calls that overlap on one GPU (on different streams, or
  *     from several host threads without ordering) race on it.
  *   - DDTREE_ERR_HIP also reports a failed lookup of the scratch's address.
  */
-#define DDTREE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+#define DDTREE_NOALLOC_SCRATCH_BYTES (72ull << 20)
 
 int ddtree_verify_attn_noalloc(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t Dl, int32_t Dr,
                                const void* q_lat, const void* q_rope,

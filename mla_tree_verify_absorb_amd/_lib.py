@@ -26,7 +26,7 @@ DDTREE_BF16 = 1
 DDTREE_MAX_NODES = 256
 DDTREE_MAX_DEPTH = 64
 DDTREE_MAX_PROPOSALS = 64
-DDTREE_NOALLOC_SCRATCH_BYTES = 64 << 20
+DDTREE_NOALLOC_SCRATCH_BYTES = 72 << 20
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32

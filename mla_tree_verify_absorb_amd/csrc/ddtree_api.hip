@@ -155,12 +155,12 @@ size_t workspace_bytes_for(bool mfma, int B, int N, int H, int Dl, int splits, i
   if (!mfma) return 0;
   if (splits == 0) {
     const int windows = band_windows_bound(B, N, H, max_prefix_len);
-    return (size_t)band_part_slots(N, H, windows) * kRowsPerBlock * (uint64_t)(Dl + 1) * sizeof(float) +
+    return (size_t)band_part_slots(N, H, windows) * kRowsPerBlock * kPartialRecordBytes +
            (size_t)windows * 4 * sizeof(int);
   }
   if (splits == 1) return 0;
   const uint64_t rows = (uint64_t)B * N * H;
-  return (size_t)(splits * rows * (uint64_t)(Dl + 1) * sizeof(float));
+  return (size_t)(splits * rows * kPartialRecordBytes);
 }
 
 // ---- scratch of ddtree_verify_attn_noalloc ----
@@ -344,18 +344,20 @@ int ddtree_verify_attn(int32_t dtype, int32_t B, int32_t N, int32_t H, int32_t D
   a.o = o;
   a.lse = lse;
   a.part_o = nullptr;
-  a.part_lse = nullptr;
+  a.part_aux = nullptr;
   a.band_edges = nullptr;
   a.band_windows = 0;
-  if (splits > 1) {
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = a.part_o + (uint64_t)splits * rows * Dl;
-  } else if (splits == 0) {
-    a.band_windows = band_windows_bound(B, N, H, max_prefix_len);
-    const uint64_t slots = (uint64_t)band_part_slots(N, H, a.band_windows);
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = a.part_o + slots * kRowsPerBlock * Dl;
-    a.band_edges = reinterpret_cast<int*>(a.part_lse + slots * kRowsPerBlock);
+  if (splits != 1) {
+    // records: fp16 values, then {lse2, k} pairs, then (band schedule) the edge descriptors
+    uint64_t records = (uint64_t)splits * rows;
+    if (splits == 0) {
+      a.band_windows = band_windows_bound(B, N, H, max_prefix_len);
+      records = (uint64_t)band_part_slots(N, H, a.band_windows) * kRowsPerBlock;
+    }
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    a.part_o = ws;
+    a.part_aux = reinterpret_cast<float2*>(ws + records * Dl * 2);
+    if (splits == 0) a.band_edges = reinterpret_cast<int*>(a.part_aux + records);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;

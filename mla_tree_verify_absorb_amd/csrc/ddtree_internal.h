@@ -35,12 +35,16 @@ struct AttnArgs {
   int balanced;        // 1: band schedule (row blocks per request a multiple or a divisor of kBandRowBlocks)
   float* o;
   float* lse;
-  // uniform schedule, splits > 1: part_o [splits][B*N*H][Dl], part_lse [splits][B*N*H]
-  // band schedule: part_o [slots][kRowsPerBlock][Dl], part_lse [slots][kRowsPerBlock] with
-  // slots = 2 * band_windows * (row blocks per band)
-  float* part_o;
-  float* part_lse;
-  int* band_edges;     // band schedule: [band_windows][4] (after part_lse): [0] the total column
+  // Partial records, one per row of a KV split or a band piece (MFMA kernel, Dl = 512):
+  //   part_o   [records][Dl] fp16: the row's unnormalised output scaled by a power of two,
+  //            in the chunk order of partial_chunk_dim (verify_attn_bf16.hip)
+  //   part_aux [records] {lse2, k}, log2 units: the record adds 2^lse2 to the merged
+  //            exp-sum and 2^k times its fp16 values to the merged numerator
+  // uniform schedule, splits > 1: [splits][B*N*H] records; band schedule: [slots][kRowsPerBlock]
+  // with slots = 2 * band_windows * (row blocks per band)
+  void* part_o;
+  float2* part_aux;
+  int* band_edges;     // band schedule: [band_windows][4] (after part_aux): [0] the total column
                        // count (int64) and the window count, [e] edge e's cut descriptor
   int band_windows;    // band schedule: most windows (host bound from the longest prefix; the
                        // kernel uses fewer when the columns run short)
@@ -61,6 +65,7 @@ constexpr int kBandXcds = 8;
 constexpr int kBandWorkgroups = kBandXcds * kBandRowBlocks;   // 256, one per CU
 constexpr int kBandMinWindowColumns = 8;   // fewest KV tile columns in a window
 constexpr int64_t kMaxBf16RowStride = int64_t(1) << 24;   // elements; keeps tile row offsets in 32 bits
+constexpr int kPartialRecordBytes = kMfmaDl * 2 + 8;       // fp16 values + {lse2, k}
 
 // KV-cache compaction (byte addressing; strides in bytes)
 struct CompactArgs {

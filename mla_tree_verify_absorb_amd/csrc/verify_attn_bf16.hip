@@ -62,6 +62,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
@@ -80,6 +81,7 @@ constexpr int C_LOADS_PER_WAVE = KT / NWAVES;   // 8 latent rows (1 KB each) per
 constexpr int LOADS_PER_WAVE = C_LOADS_PER_WAVE + 1;  // + one 1 KB slice of the rotary region
 constexpr int MAXW = 8;                     // mask words per row (N <= 256)
 constexpr float kHeadroomLog2 = 100.0f;     // scores may exceed a row's reference by 2^100
+constexpr int kPartialTopExp = 14;          // partial records: a row's largest |value| in [2^13, 2^14)
 constexpr bf16x2 kBf16Ones = {(__bf16)1.0f, (__bf16)1.0f};
 
 static_assert(KT * R_ROW == NWAVES * 1024, "rotary region must split into one 1 KB load per wave");
@@ -926,6 +928,10 @@ verify_attn_bf16_kernel(AttnArgs a) {
           m_max = fmaxf(m_max, m_abs + mx);
           overflow |= mx > kHeadroomLog2;
         }
+        // Keep each step's share of the P pipeline next to its MFMA: left free,
+        // the scheduler bunches these VALU instructions between a few MFMAs, in
+        // a pattern that shifts with code elsewhere in the kernel.
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     pb[0] = pn[0];
@@ -943,57 +949,106 @@ verify_attn_bf16_kernel(AttnArgs a) {
 
   // ---- epilogue ----
   const float l_tot = halves_sum(l_run);
-  const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-  if (row_ok) {
-  float* orow = (to_part ? a.part_o : a.o) + (dest0 + row_local) * DL;
-  float* lrow = (to_part ? a.part_lse : a.lse) + dest0 + row_local;
-  // oacc[db][4 jj + i] is dim 32 db + 8 jj + 4 g + i of row lr
+  if (row_ok && !to_part) {
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    float* orow = a.o + (dest0 + row_local) * DL;
+    // oacc[db][4 jj + i] is dim 32 db + 8 jj + 4 g + i of row lr
 #pragma unroll
-  for (int db = 0; db < DL / 32; ++db) {
+    for (int db = 0; db < DL / 32; ++db) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float4 v;
-      v.x = oacc[db][4 * jj + 0] * inv_l;
-      v.y = oacc[db][4 * jj + 1] * inv_l;
-      v.z = oacc[db][4 * jj + 2] * inv_l;
-      v.w = oacc[db][4 * jj + 3] * inv_l;
-      *reinterpret_cast<float4*>(orow + 32 * db + 8 * jj + 4 * g) = v;
+      for (int jj = 0; jj < 4; ++jj) {
+        float4 v;
+        v.x = oacc[db][4 * jj + 0] * inv_l;
+        v.y = oacc[db][4 * jj + 1] * inv_l;
+        v.z = oacc[db][4 * jj + 2] * inv_l;
+        v.w = oacc[db][4 * jj + 3] * inv_l;
+        *reinterpret_cast<float4*>(orow + 32 * db + 8 * jj + 4 * g) = v;
+      }
     }
-  }
-  if (g == 0) *lrow = lse;
+    if (g == 0) a.lse[dest0 + row_local] = lse;
+  } else if (row_ok) {
+    // Partial record (see partial_chunk_dims): the unnormalised output in fp16,
+    // scaled by 2^(14 - e) so that the row's largest magnitude lies in [2^13,
+    // 2^14), and {lse2, k} in log2 units: the piece adds 2^lse2 to the merged
+    // exp-sum and 2^k times the stored values to the merged numerator.
+    float amax = 0.f;
+#pragma unroll
+    for (int db = 0; db < DL / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(oacc[db][e]));
+    amax = halves_max(amax);
+    int ex = 0;
+    if (amax <= 3.4e38f) frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1); 0, inf, NaN: ex = 0
+    const int sh = kPartialTopExp - ex;
+    f16x8* prow = reinterpret_cast<f16x8*>(static_cast<_Float16*>(a.part_o) + (dest0 + row_local) * DL);
+    // chunk 4 db + 2 jp + g of the row is oacc[db][8 jp .. 8 jp + 7] of lane (lr, g)
+#pragma unroll
+    for (int db = 0; db < DL / 32; ++db) {
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+        f16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (_Float16)ldexpf(oacc[db][8 * jp + i], sh);
+        prow[4 * db + 2 * jp + g] = v;
+      }
+    }
+    if (g == 0) {
+      const bool seen = l_tot > 0.f;
+      a.part_aux[dest0 + row_local] =
+          make_float2(seen ? m_ref + log2f(l_tot) : -INFINITY, seen ? m_ref - (float)sh : -INFINITY);
+    }
   }
   }   // pieces
 }
 
-// Merge split partials: lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.
-__global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse, int splits,
-                                                           int64_t total_rows, int Dl, float* __restrict__ o,
+// Partial records: dims of fp16 chunk c (8 values) of a row.  Values 0..3 are
+// dims 32 db + 16 jp + 4 gg + (0..3), values 4..7 the same + 8, with db = c / 4,
+// jp = (c / 2) % 2, gg = c % 2 (the order the attention kernel's lanes hold them).
+__device__ __forceinline__ int partial_chunk_dim(int c) { return 32 * (c >> 2) + 16 * ((c >> 1) & 1) + 4 * (c & 1); }
+
+// Adds w times fp16 chunk v (dims partial_chunk_dim(c) + 0..3 and + 8..11) into acc[0], acc[1].
+__device__ __forceinline__ void partial_chunk_fma(float4 (&acc)[2], float w, const f16x8& v) {
+  acc[0].x += w * (float)v[0];
+  acc[0].y += w * (float)v[1];
+  acc[0].z += w * (float)v[2];
+  acc[0].w += w * (float)v[3];
+  acc[1].x += w * (float)v[4];
+  acc[1].y += w * (float)v[5];
+  acc[1].z += w * (float)v[6];
+  acc[1].w += w * (float)v[7];
+}
+
+// Merge split partials (records as written by the attention kernel's epilogue):
+// with M = max_s lse2_s, o = sum_s 2^(k_s - M) v_s / sum_s 2^(lse2_s - M) and
+// lse = (M + log2 sum_s 2^(lse2_s - M)) ln 2.  One thread per (row, fp16 chunk).
+__global__ void __launch_bounds__(256) attn_combine_kernel(const _Float16* __restrict__ part_o,
+                                                           const float2* __restrict__ part_aux, int splits,
+                                                           int64_t total_rows, float* __restrict__ o,
                                                            float* __restrict__ lse) {
-  const int per_row = Dl / 4;
+  constexpr int per_row = DL / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = idx / per_row;
-  const int c4 = (int)(idx - row * per_row);
+  const int c = (int)(idx - row * per_row);
   if (row >= total_rows) return;
   float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_lse[s * total_rows + row]);
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_aux[s * total_rows + row].x);
   float wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < splits; ++s) {
-    const float ls = part_lse[s * total_rows + row];
-    if (ls == -INFINITY) continue;
-    const float w = expf(ls - mx);
-    wsum += w;
-    const float4 v = reinterpret_cast<const float4*>(part_o + (s * total_rows + row) * Dl)[c4];
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+  float4 acc[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  if (mx != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float2 ax = part_aux[s * total_rows + row];
+      if (ax.x == -INFINITY) continue;   // an empty split: exp-sum 0, output 0
+      wsum += exp2f(ax.x - mx);
+      partial_chunk_fma(acc, exp2f(ax.y - mx),
+                        reinterpret_cast<const f16x8*>(part_o + (s * total_rows + row) * DL)[c]);
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  reinterpret_cast<float4*>(o + row * Dl)[c4] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (c4 == 0) lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  float* orow = o + row * DL + partial_chunk_dim(c);
+  *reinterpret_cast<float4*>(orow) = make_float4(acc[0].x * inv, acc[0].y * inv, acc[0].z * inv, acc[0].w * inv);
+  *reinterpret_cast<float4*>(orow + 8) = make_float4(acc[1].x * inv, acc[1].y * inv, acc[1].z * inv, acc[1].w * inv);
+  if (c == 0) lse[row] = wsum > 0.f ? (mx + log2f(wsum)) * 0.6931471805599453f : -INFINITY;
 }
 
 // Band schedule: merge the pieces of every band cut by a window edge.
@@ -1001,10 +1056,25 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 // blocks per band): if the band at edge e is cut there first (the attention
 // kernel's descriptor), rows 8 g .. 8 g + 7 of its row block j, from the tail
 // piece of window e - 1 and the head pieces of windows e .. last (no window is
-// empty).  32 threads per row, 4 float4 columns each; lane i of a row reads the
-// log-sum-exp of pieces i, i + 32, ..., so the weights need no serial loads.
+// empty).  32 threads per row, fp16 chunks c0 and c0 + 32 each; lane i of a row
+// reads the records of pieces i, i + 32, ..., so the weights need no serial loads.
 constexpr int kCombineRowsPerGroup = 8;
 constexpr int kCombineGroups = ROWS / kCombineRowsPerGroup;
+constexpr int kCombinePiecesInFlight = 8;   // 2 chunk loads each
+
+__device__ __forceinline__ void store_merged_row(const AttnArgs& a, int64_t grow, int c0, const float4 (&acc)[2][2],
+                                                 float wsum, float mx) {
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float* orow = a.o + grow * DL + partial_chunk_dim(c0 + 32 * h);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<float4*>(orow + 8 * q) =
+          make_float4(acc[h][q].x * inv, acc[h][q].y * inv, acc[h][q].z * inv, acc[h][q].w * inv);
+  }
+  if (c0 == 0) a.lse[grow] = wsum > 0.f ? (mx + log2f(wsum)) * 0.6931471805599453f : -INFINITY;
+}
 
 __global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
   const int n_rows = a.N * a.H;
@@ -1022,65 +1092,59 @@ __global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
   const int r = (kb * rbb + j) * ROWS + rl;
   if (r >= n_rows) return;
   const int c0 = threadIdx.x & 31;
-  auto piece_slot = [&](int i) { return band_part_slot(e - 1 + i, j, rbb, i > 0); };
+  const _Float16* part = static_cast<const _Float16*>(a.part_o);
+  auto piece_rec = [&](int i) { return (int64_t)band_part_slot(e - 1 + i, j, rbb, i > 0) * ROWS + rl; };
   float mx = -INFINITY;
-  for (int i = c0; i < n_pc; i += 32) mx = fmaxf(mx, a.part_lse[piece_slot(i) * ROWS + rl]);
+  for (int i = c0; i < n_pc; i += 32) mx = fmaxf(mx, a.part_aux[piece_rec(i)].x);
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
   float wsum = 0.f;
-  float4 acc[4];
+  float4 acc[2][2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0; i0 < n_pc; i0 += 32) {
-    // an empty piece (lse -inf) has o = 0 and weight 0
-    float wl = 0.f;
-    if (i0 + c0 < n_pc && mx != -INFINITY) wl = expf(a.part_lse[piece_slot(i0 + c0) * ROWS + rl] - mx);
-    float ws = wl;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 32);
-    wsum += ws;
-    const int n = min(32, n_pc - i0);
-    // 4 pieces at a time (16 loads in flight); a piece past the end re-reads
-    // piece ii with weight 0
-    for (int ii = 0; ii < n; ii += 4) {
-      float w[4];
-      float4 v[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        w[u] = __shfl(wl, ii + u, 32);
-        const bool ok = ii + u < n;
-        if (!ok) w[u] = 0.f;
-        const float4* src =
-            reinterpret_cast<const float4*>(a.part_o + ((int64_t)piece_slot(i0 + (ok ? ii + u : ii)) * ROWS + rl) * DL);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[u][k] = src[c0 + 32 * k];
+  for (int h = 0; h < 2; ++h) acc[h][0] = acc[h][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (mx != -INFINITY) {
+    for (int i0 = 0; i0 < n_pc; i0 += 32) {
+      // an empty piece (lse2 -inf) has weight 0 (its stored values are 0)
+      float wl = 0.f, wk = 0.f;
+      if (i0 + c0 < n_pc) {
+        const float2 ax = a.part_aux[piece_rec(i0 + c0)];
+        wl = exp2f(ax.x - mx);
+        wk = exp2f(ax.y - mx);
       }
+      float ws = wl;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int off = 16; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 32);
+      wsum += ws;
+      const int n = min(32, n_pc - i0);
+      // kCombinePiecesInFlight pieces at a time; a piece past the end re-reads piece ii with weight 0
+      for (int ii = 0; ii < n; ii += kCombinePiecesInFlight) {
+        float w[kCombinePiecesInFlight];
+        f16x8 v[kCombinePiecesInFlight][2];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          acc[k].x += w[u] * v[u][k].x;
-          acc[k].y += w[u] * v[u][k].y;
-          acc[k].z += w[u] * v[u][k].z;
-          acc[k].w += w[u] * v[u][k].w;
+        for (int u = 0; u < kCombinePiecesInFlight; ++u) {
+          const bool ok = ii + u < n;
+          w[u] = ok ? __shfl(wk, ii + u, 32) : 0.f;
+          const f16x8* src = reinterpret_cast<const f16x8*>(part + piece_rec(i0 + (ok ? ii + u : ii)) * DL);
+          v[u][0] = src[c0];
+          v[u][1] = src[c0 + 32];
         }
+#pragma unroll
+        for (int u = 0; u < kCombinePiecesInFlight; ++u) {
+          partial_chunk_fma(acc[0], w[u], v[u][0]);
+          partial_chunk_fma(acc[1], w[u], v[u][1]);
+        }
+      }
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int64_t grow = (int64_t)b * n_rows + r;
-  float4* dst = reinterpret_cast<float4*>(a.o + grow * DL);
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    dst[c0 + 32 * k] = make_float4(acc[k].x * inv, acc[k].y * inv, acc[k].z * inv, acc[k].w * inv);
-  if (c0 == 0) a.lse[grow] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  store_merged_row(a, (int64_t)b * n_rows + r, c0, acc, wsum, mx);
 }
 
 // Band schedule with small bands (R < 32): a cut band has few rows and may have
 // hundreds of pieces (one request, one row block, 256 windows), so the four
-// waves of a workgroup split the pieces of 2 rows, 4 pieces at a time (16 float4
-// loads in flight per lane), with weights against the max over all the pieces;
-// the waves' sums are added through LDS.  Same (edge, slot) pairs as above, 64
-// groups of 2 rows per row block.
+// waves of a workgroup split the pieces of 2 rows, kCombinePiecesInFlight at a
+// time, with weights against the max over all the pieces; the waves' sums are
+// added through LDS.  Same (edge, slot) pairs as above, 64 groups of 2 rows per
+// row block.
 constexpr int kSplitRows = 2;
 constexpr int kSplitGroups = ROWS / kSplitRows;
 
@@ -1105,68 +1169,65 @@ __global__ void __launch_bounds__(256) attn_band_combine_split_kernel(AttnArgs a
   if ((kb * rbb + j) * ROWS + grp * kSplitRows >= n_rows) return;   // the whole group is past the end
   const bool row_ok = r < n_rows;
   const int c0 = lane & 31;
-  auto piece_slot = [&](int i) { return band_part_slot(e - 1 + i, j, rbb, i > 0); };
+  const _Float16* part = static_cast<const _Float16*>(a.part_o);
+  auto piece_rec = [&](int i) { return (int64_t)band_part_slot(e - 1 + i, j, rbb, i > 0) * ROWS + rl; };
   float mx = -INFINITY;
-  for (int i = c0; i < n_pc; i += 32) mx = fmaxf(mx, a.part_lse[piece_slot(i) * ROWS + rl]);
+  for (int i = c0; i < n_pc; i += 32) mx = fmaxf(mx, a.part_aux[piece_rec(i)].x);
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
   float wsum = 0.f;
-  float4 acc[4];
+  float4 acc[2][2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  // wave w takes pieces 4 q .. 4 q + 3 for q = w, w + 4, ...; a piece past the end
-  // re-reads piece 4 q with weight 0, an empty piece (lse -inf) has o = 0 and weight 0
-  for (int i0 = 4 * wave; i0 < n_pc; i0 += 16) {
-    float w[4];
-    float4 v[4][4];
+  for (int h = 0; h < 2; ++h) acc[h][0] = acc[h][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // wave w takes pieces P q .. P q + P - 1 for q = w, w + 4, ... (P pieces in flight); a piece
+  // past the end re-reads piece P q with weight 0, an empty piece (lse2 -inf) has weight 0
+  constexpr int P = kCombinePiecesInFlight;
+  if (mx != -INFINITY) {
+    for (int i0 = P * wave; i0 < n_pc; i0 += 4 * P) {
+      float w[P];
+      f16x8 v[P][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool ok = i0 + u < n_pc;
-      const int slot = piece_slot(ok ? i0 + u : i0);
-      const float ls = a.part_lse[slot * ROWS + rl];
-      w[u] = ok && mx != -INFINITY ? expf(ls - mx) : 0.f;
-      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((int64_t)slot * ROWS + rl) * DL);
+      for (int u = 0; u < P; ++u) {
+        const bool ok = i0 + u < n_pc;
+        const int64_t rec = piece_rec(ok ? i0 + u : i0);
+        const float2 ax = a.part_aux[rec];
+        wsum += ok ? exp2f(ax.x - mx) : 0.f;
+        w[u] = ok ? exp2f(ax.y - mx) : 0.f;
+        const f16x8* src = reinterpret_cast<const f16x8*>(part + rec * DL);
+        v[u][0] = src[c0];
+        v[u][1] = src[c0 + 32];
+      }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[u][k] = src[c0 + 32 * k];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      wsum += w[u];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[k].x += w[u] * v[u][k].x;
-        acc[k].y += w[u] * v[u][k].y;
-        acc[k].z += w[u] * v[u][k].z;
-        acc[k].w += w[u] * v[u][k].w;
+      for (int u = 0; u < P; ++u) {
+        partial_chunk_fma(acc[0], w[u], v[u][0]);
+        partial_chunk_fma(acc[1], w[u], v[u][1]);
       }
     }
   }
   if (wave > 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) s_acc[wave - 1][lane][k] = acc[k];
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) s_acc[wave - 1][lane][2 * h + q] = acc[h][q];
     s_w[wave - 1][lane] = wsum;
   }
   __syncthreads();
   if (wave > 0 || !row_ok) return;
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    wsum += s_w[q][lane];
+  for (int w = 0; w < 3; ++w) {
+    wsum += s_w[w][lane];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float4 t = s_acc[q][lane][k];
-      acc[k].x += t.x;
-      acc[k].y += t.y;
-      acc[k].z += t.z;
-      acc[k].w += t.w;
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float4 t = s_acc[w][lane][2 * h + q];
+        acc[h][q].x += t.x;
+        acc[h][q].y += t.y;
+        acc[h][q].z += t.z;
+        acc[h][q].w += t.w;
+      }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int64_t grow = (int64_t)b * n_rows + r;
-  float4* dst = reinterpret_cast<float4*>(a.o + grow * DL);
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    dst[c0 + 32 * k] = make_float4(acc[k].x * inv, acc[k].y * inv, acc[k].z * inv, acc[k].w * inv);
-  if (c0 == 0) a.lse[grow] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  store_merged_row(a, (int64_t)b * n_rows + r, c0, acc, wsum, mx);
 }
 
 }  // namespace
@@ -1181,11 +1242,11 @@ hipError_t launch_verify_attn_bf16(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream) {
   const int64_t total_rows = (int64_t)a.B * a.N * a.H;
-  const int64_t threads = total_rows * (a.Dl / 4);
+  const int64_t threads = total_rows * (DL / 8);
   const int64_t blocks = (threads + 255) / 256;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.part_o, a.part_lse,
-                     a.splits, total_rows, a.Dl, a.o, a.lse);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const _Float16*>(a.part_o), a.part_aux, a.splits, total_rows, a.o, a.lse);
   return hipGetLastError();
 }
 

@@ -133,18 +133,18 @@ static void check_verify_attn(void) {
   /* workspace */
   c = attn_defaults(); c.splits = 4; EXPECT(attn(c), DDTREE_ERR_WORKSPACE);
   c = attn_defaults(); c.N = 64; c.splits = 0; EXPECT(attn(c), DDTREE_ERR_WORKSPACE);
-  c = attn_defaults(); c.splits = 4; c.ws = A + (8u << 24); c.ws_bytes = (size_t)4 * 8 * 64 * 513 * 4 - 4;
+  c = attn_defaults(); c.splits = 4; c.ws = A + (8u << 24); c.ws_bytes = (size_t)4 * 8 * 64 * 1032 - 4;
   EXPECT(attn(c), DDTREE_ERR_WORKSPACE);
-  c = attn_defaults(); c.splits = 4; c.ws = A + (8u << 24) + 8; c.ws_bytes = (size_t)4 * 8 * 64 * 513 * 4;
+  c = attn_defaults(); c.splits = 4; c.ws = A + (8u << 24) + 8; c.ws_bytes = (size_t)4 * 8 * 64 * 1032;
   EXPECT(attn(c), DDTREE_ERR_INVALID_ARG);
-  c = attn_defaults(); c.splits = 4; c.ws = A + (2u << 24) + 32; c.ws_bytes = (size_t)4 * 8 * 64 * 513 * 4;
+  c = attn_defaults(); c.splits = 4; c.ws = A + (2u << 24) + 32; c.ws_bytes = (size_t)4 * 8 * 64 * 1032;
   EXPECT(attn(c), DDTREE_ERR_INVALID_ARG);
   c = attn_defaults(); c.splits = 4; c.ws = UINTPTR_MAX - 4095; c.ws_bytes = SIZE_MAX;
   EXPECT(attn(c), DDTREE_ERR_INVALID_ARG);
 
   /* the no-allocation variant refuses what its scratch cannot hold, before any HIP call */
-  c = attn_defaults(); c.N = 64; c.splits = 0; c.max_len = 4096; EXPECT(attn_noalloc(c), DDTREE_ERR_WORKSPACE);
-  c = attn_defaults(); c.N = 64; c.splits = 16; c.max_len = 4096; EXPECT(attn_noalloc(c), DDTREE_ERR_WORKSPACE);
+  c = attn_defaults(); c.N = 64; c.splits = 18; c.max_len = 4096; EXPECT(attn_noalloc(c), DDTREE_ERR_WORKSPACE);
+  c = attn_defaults(); c.N = 64; c.splits = 1024; c.max_len = 4096; EXPECT(attn_noalloc(c), DDTREE_ERR_WORKSPACE);
   c = attn_defaults(); c.B = 0; EXPECT(attn_noalloc(c), DDTREE_OK);
   c = attn_defaults(); c.q = 0; EXPECT(attn_noalloc(c), DDTREE_ERR_INVALID_ARG);
   c = attn_defaults(); c.max_len = INT64_MAX; EXPECT(attn_noalloc(c), DDTREE_ERR_UNSUPPORTED);

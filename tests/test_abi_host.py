@@ -129,28 +129,28 @@ def test_verify_attn_rejects_aliasing():
     # rotary rows (1024 bytes in, 128 bytes each) 73728
     assert attn(o=A + (2 << 24) + 4096) == INVALID            # o inside the latent rows
     assert attn(lse=A + (2 << 24) + 73650) == INVALID         # lse inside the last rotary row only
-    assert attn(splits=4, ws=A + (2 << 24) + 32, ws_bytes=4 * 8 * 64 * 513 * 4) == INVALID   # workspace
+    assert attn(splits=4, ws=A + (2 << 24) + 32, ws_bytes=4 * 8 * 64 * 1032) == INVALID   # workspace
 
 
 def test_workspace_contract():
     lib = dd.lib()
-    # splits = 1 needs no workspace; S > 1 needs S * rows * (Dl + 1) floats
+    # splits = 1 needs no workspace; S > 1 needs S * rows records of 2 Dl + 8 bytes (fp16 values, two floats)
     assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 8, 64, 512, 64, 4096, 1) == 0
-    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 8, 64, 512, 64, 4096, 4) == 4 * 8 * 64 * 513 * 4
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 8, 64, 512, 64, 4096, 4) == 4 * 8 * 64 * 1032
     assert lib.ddtree_verify_attn_workspace_size(F32, 1, 8, 4, 64, 32, 4096, 4) == 0   # fp32 path never splits
     assert attn(splits=4) == WORKSPACE
-    assert attn(splits=4, ws=A + (8 << 24), ws_bytes=4 * 8 * 64 * 513 * 4 - 4) == WORKSPACE
-    assert attn(splits=4, ws=A + (8 << 24) + 8, ws_bytes=4 * 8 * 64 * 513 * 4) == INVALID   # misaligned
+    assert attn(splits=4, ws=A + (8 << 24), ws_bytes=4 * 8 * 64 * 1032 - 4) == WORKSPACE
+    assert attn(splits=4, ws=A + (8 << 24) + 8, ws_bytes=4 * 8 * 64 * 1032) == INVALID   # misaligned
     assert attn(splits=-1) == INVALID
 
 
 def band_ws(R, W, Dl=512):
     """Band workspace for R row blocks per band and a bound of W windows: (window, slot, head/tail) partial
-    slots of 128 rows x (Dl + 1) floats, then W records of 4 ints."""
-    return 2 * W * R * 128 * (Dl + 1) * 4 + 16 * W
+    slots of 128 row records (Dl fp16 values and two floats), then W records of 4 ints."""
+    return 2 * W * R * 128 * (2 * Dl + 8) + 16 * W
 
 
-BAND_WS = band_ws(32, 8)      # 32 row blocks per band, 8 windows: 134.5 MB
+BAND_WS = band_ws(32, 8)      # 32 row blocks per band, 8 windows: 67.6 MB
 
 
 def test_auto_schedule():
@@ -172,7 +172,7 @@ def test_auto_schedule():
     # otherwise uniform splits: enough workgroups to cover 256 CUs, at least 4 tiles per split
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 24, 64, 512, 64, 4096) == 22      # 12 row blocks: 256 / 12
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 40, 64, 512, 64, 4096) == 13      # 20 row blocks
-    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 40, 64, 512, 64, 4096, 0) == 13 * 40 * 64 * 513 * 4
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 40, 64, 512, 64, 4096, 0) == 13 * 40 * 64 * 1032
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 24, 64, 512, 64, 32) == 1         # 2 tiles: no split
     assert lib.ddtree_verify_attn_auto_splits(BF16, 1, 3, 128, 512, 64, 4096) == 32      # 3 row blocks: 86, capped at 129 / 4
     assert lib.ddtree_verify_attn_auto_splits(BF16, 9, 40, 64, 512, 64, 4096) == 2       # 180 row blocks
@@ -184,7 +184,7 @@ def test_auto_schedule():
     assert lib.ddtree_verify_attn_workspace_size(F32, 1, 64, 64, 64, 32, 4096, 0) == 0
     # an explicit split count always takes the uniform schedule
     assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 1) == 0
-    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 8) == 8 * 64 * 64 * 513 * 4
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 8) == 8 * 64 * 64 * 1032
     # the band schedule needs its workspace like any split
     assert attn(N=64, splits=0) == WORKSPACE
     assert attn(N=64, splits=0, ws=A + (8 << 24), ws_bytes=band_ws(32, 1) - 4) == WORKSPACE   # max_len 64: 1 window
@@ -196,7 +196,7 @@ def test_band_workspace_is_sized_from_the_call():
     # the K2 workloads: 32 row blocks per band, 8 windows (the most for R = 32)
     assert ws(1, 64, 64, 4096) == ws(16, 64, 64, 32768) == ws(4, 128, 64, 131072) == band_ws(32, 8)
     # small requests: 130 columns / 8 = 16 windows (R = 1 or 4), far below the K2 size
-    assert ws(1, 16, 8, 4096) == band_ws(1, 16) == 8405248
+    assert ws(1, 16, 8, 4096) == band_ws(1, 16) == 4227328
     assert ws(1, 64, 8, 4096) == band_ws(4, 16)
     # the bound follows max_prefix_len: a 64-node, 64-head request with no prefix has 2 columns, one window
     assert ws(1, 64, 64, 0) == band_ws(32, 1)
@@ -217,14 +217,18 @@ def attn_noalloc(**kw):
 
 
 def test_noalloc_rejects_what_its_scratch_cannot_hold():
-    """Checked before anything touches the device: a shape whose workspace exceeds the 64 MiB scratch is
+    """Checked before anything touches the device: a shape whose workspace exceeds the 72 MiB scratch is
     refused with DDTREE_ERR_WORKSPACE, and invalid arguments keep ddtree_verify_attn's errors."""
     lib = dd.lib()
-    assert dd.DDTREE_NOALLOC_SCRATCH_BYTES == 64 << 20
-    big = lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 0)
-    assert big > dd.DDTREE_NOALLOC_SCRATCH_BYTES
-    assert attn_noalloc(N=64, splits=0, max_len=4096) == WORKSPACE         # 64 nodes x 64 heads, 4096 tokens
-    assert attn_noalloc(N=64, splits=16, max_len=4096) == WORKSPACE        # 16 uniform splits of 4096 rows
+    assert dd.DDTREE_NOALLOC_SCRATCH_BYTES == 72 << 20
+    # the band schedule's largest workspace (32 row blocks per band, 8 windows) fits
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 0) == BAND_WS
+    assert BAND_WS <= dd.DDTREE_NOALLOC_SCRATCH_BYTES
+    # 64 nodes x 64 heads: 17 uniform splits fit, 18 do not
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 17) <= dd.DDTREE_NOALLOC_SCRATCH_BYTES
+    assert lib.ddtree_verify_attn_workspace_size(BF16, 1, 64, 64, 512, 64, 4096, 18) > dd.DDTREE_NOALLOC_SCRATCH_BYTES
+    assert attn_noalloc(N=64, splits=18, max_len=4096) == WORKSPACE
+    assert attn_noalloc(N=64, splits=64, max_len=4096) == WORKSPACE
     assert attn_noalloc(B=0) == OK
     assert attn_noalloc(N=0) == INVALID
     assert attn_noalloc(q=None) == INVALID                                 # splits=1: no scratch needed
