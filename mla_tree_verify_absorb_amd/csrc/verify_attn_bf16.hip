@@ -510,6 +510,12 @@ __device__ __forceinline__ void band_cursor_next(const AttnArgs& a, PieceCursor&
 
 constexpr int KRING = 4;   // K-fragment reads in flight ahead of the S^T MFMAs
 constexpr int QREG = DL / 16 - 4;   // latent query k-steps held in VGPRs; the last 4 are staged in LDS
+constexpr int kQRowBytes = QREG * 32;                  // 896: a row's VGPR k-steps
+constexpr int kQRowChunks = kQRowBytes / 16;           // 56
+constexpr int kQRegionBytes = 32 * kQRowBytes;         // a wave's 32 rows: 28 KB
+constexpr int kPloBytes = NWAVES * 64 * 32;
+static_assert(NWAVES * kQRegionBytes <= NBUF * TILE_BYTES + kPloBytes, "the query copy fits the ring and s_plo");
+static_assert(kQRegionBytes % 1024 == 0 && kQRowChunks % 8 == 0, "whole 1 KB copies; the chunk swizzle stays in a row");
 static_assert(DL / 16 - QREG == DR / 16, "the staged latent queries use the rotary pair-row layout");
 constexpr int VRING = 3;   // V^T-fragment reads (pairs) in flight ahead of the O^T MFMAs
 // s_waitcnt operand: lgkmcnt(n), no vmcnt or expcnt wait
@@ -537,13 +543,15 @@ static_assert(NST - O_HEAD >= 20, "the P pipeline needs 20 O^T steps");
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 verify_attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char s_kv[NBUF * TILE_BYTES];
+  // the KV ring, then the second-term buffer s_plo (one array: the query copy at
+  // the start of a piece uses the first NWAVES * kQRegionBytes bytes of both)
+  __shared__ __attribute__((aligned(1024))) unsigned char s_kv[NBUF * TILE_BYTES + kPloBytes];
   __shared__ uint32_t s_mask[ROWS][MAXW];
   // queries of the last QREG_LDS latent k-steps (part 0) and the rotary ones (part 1), swizzled pair rows
   __shared__ __attribute__((aligned(16))) unsigned char s_qx[2 * ROWS * R_ROW];
   __shared__ PieceCursor s_cur;
   // second bf16 term of P of one tile, per lane, in the lane's B-operand layout
-  __shared__ __attribute__((aligned(16))) unsigned char s_plo[NWAVES * 64 * 32];
+  unsigned char* const s_plo = s_kv + NBUF * TILE_BYTES;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -651,26 +659,60 @@ verify_attn_bf16_kernel(AttnArgs a) {
   // in the rotary pair-row layout (row rl at pair row rl >> 1) and read per tile.
   const int r_loc = rb * ROWS + wave * 32 + lr;
   const bool row_ok = r_loc < n_rows;
-  const int64_t grow = (int64_t)b * n_rows + (row_ok ? r_loc : 0);
   const int row_local = wave * 32 + lr;
   bf16x8 qf[QREG];
   {
-    const bf16x8* ql = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q_lat) + grow * DL) + g;
+    // Each wave copies its own 32 rows into LDS with direct-to-LDS loads (1 KB
+    // of consecutive 16-byte chunks per load): the k-steps held in VGPRs into
+    // a kQRegionBytes region at the start of the ring (row rr at kQRowBytes rr,
+    // its chunk q at position q ^ (rr & 7)), the staged k-steps and the rotary
+    // part straight into s_qx (the wave's rows are pair rows 16 wave .. 16 wave
+    // + 15 there, 4 KB a part).  Rows past the request's last row re-read its
+    // last row, and their fragments are zeroed once the copies have landed.
+    const int w_row0 = rb * ROWS + wave * 32;          // wave-uniform
+    const int w_base = min(w_row0, n_rows - 1);
+    const int w_last = n_rows - 1 - w_base;            // rows of the wave that exist, less one
+    const int64_t brow = (int64_t)b * n_rows + w_base;
+    const unsigned char* qlb = static_cast<const unsigned char*>(a.q_lat) + brow * (DL * 2);
+    const unsigned char* qrb = static_cast<const unsigned char*>(a.q_rope) + brow * (DR * 2);
+    // (lane values go through opaque() so that they are computed here, not
+    // hoisted out of the piece loop and spilled)
+    const uint32_t region = lds0 + (uint32_t)(wave * kQRegionBytes);
 #pragma unroll
-    for (int s = 0; s < DL / 16; ++s) {
-      const bf16x8 v0 = ql[2 * s];
-      const bf16x8 v = row_ok ? v0 : bf16x8{};
-      if (s < QREG)
-        qf[s] = v;
-      else
-        *reinterpret_cast<bf16x8*>(s_qx + (row_local >> 1) * 256 + (pair_chunk(row_local, 2 * (s - QREG) + g) << 4)) = v;
+    for (int i = 0; i < kQRegionBytes / 1024; ++i) {
+      const int c = 64 * i + opaque(lane);
+      const int rr = c / kQRowChunks;
+      const int q = (c - rr * kQRowChunks) ^ (rr & 7);
+      lds_dma16_rotary(region + 1024 * i, qlb, (uint32_t)(min(rr, w_last) * (DL * 2)), (uint32_t)(q * 16));
     }
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q_rope) + grow * DR);
+    const uint32_t sqx = (uint32_t)(uintptr_t)(lds_void_t*)s_qx + (uint32_t)(wave * 4096);
 #pragma unroll
-    for (int c = g; c < DR / 8; c += 2) {
-      const bf16x8 v0 = qr[c];
-      const bf16x8 v = row_ok ? v0 : bf16x8{};
-      *reinterpret_cast<bf16x8*>(s_qx + ROWS * R_ROW + (row_local >> 1) * 256 + (pair_chunk(row_local, c) << 4)) = v;
+    for (int j = 0; j < 4; ++j) {
+      const int ln = opaque(lane);
+      const int pr = 16 * wave + 4 * j + (ln >> 4);
+      const int logical = (ln & 15) ^ (pr & 7);
+      const int rr = min(2 * pr + (logical >> 3) - 32 * wave, w_last);
+      const uint32_t piece = (uint32_t)((logical & 7) * 16);
+      lds_dma16_rotary(sqx + 1024 * j, qlb, (uint32_t)(rr * (DL * 2)), piece + QREG * 32);
+      lds_dma16_rotary(sqx + ROWS * R_ROW + 1024 * j, qrb, (uint32_t)(rr * (DR * 2)), piece);
+    }
+    wait_copies();   // this wave's copies have landed
+    // chunk 2 s + g of row lr sits at 128 (s >> 2) + 16 ((2 (s & 3) + g) ^ (lr & 7)):
+    // four lane bases, the rest immediate offsets
+    const int lro = opaque(lr);
+    const unsigned char* qrow = s_kv + wave * kQRegionBytes + lro * kQRowBytes;
+#pragma unroll
+    for (int s = 0; s < QREG; ++s) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + (((2 * (s & 3) + g) ^ (lro & 7)) << 4) + (s >> 2) * 128);
+      qf[s] = row_ok ? v : bf16x8{};
+    }
+    if (!row_ok) {
+#pragma unroll
+      for (int c = g; c < 8; c += 2) {
+        *reinterpret_cast<bf16x8*>(s_qx + (row_local >> 1) * 256 + (pair_chunk(row_local, c) << 4)) = bf16x8{};
+        *reinterpret_cast<bf16x8*>(s_qx + ROWS * R_ROW + (row_local >> 1) * 256 + (pair_chunk(row_local, c) << 4)) =
+            bf16x8{};
+      }
     }
   }
 
@@ -689,7 +731,9 @@ verify_attn_bf16_kernel(AttnArgs a) {
   float l_run = 0.f;         // this lane's half of the row's exp-sum
   const float c_log2 = a.scale * 1.4426950408889634f;
 
-  // Ring slot 2 starts zeroed: the first PV of a pass runs on it with a zero P.
+  // Ring slot 2 starts zeroed: the first PV of a pass runs on it with a zero P
+  // (once every wave has read its queries out of the ring).
+  __syncthreads();
   for (int i = tid; i < TILE_BYTES / 16; i += 256)
     reinterpret_cast<uint4*>(s_kv + 2 * TILE_BYTES)[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
