@@ -402,6 +402,7 @@ struct PieceCursor {
   int win, slot;     // window and row block within each band
   int64_t S;         // first column of request b
   int64_t X0, X1;    // the window's columns
+  int64_t p0, L;     // request b's first cache row and prefix length
 };
 
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
@@ -425,6 +426,8 @@ __device__ __forceinline__ PieceCursor uniform_cursor(const PieceCursor& v) {
   c.S = uniform64(v.S);
   c.X0 = uniform64(v.X0);
   c.X1 = uniform64(v.X1);
+  c.p0 = uniform64(v.p0);
+  c.L = uniform64(v.L);
   return c;
 }
 
@@ -438,7 +441,29 @@ __device__ PieceCursor band_cursor_start(const AttnArgs& a, int n_rb, int block)
   c.rbb = band_row_blocks(n_rb);
   c.nb = n_rb / c.rbb;
   c.ntt = (a.N + KT - 1) / KT;
-  const int64_t C = uniform64(band_columns_total(a.prefix_offsets, a.B, c.nb, c.ntt));
+  // Up to 64 requests: lane l loads request l's bounds once, and the column
+  // total, the search for the window's first request and that request's bounds
+  // all come from those registers.  More requests: scans in chunks of 64.
+  const bool one_chunk = a.B <= 64;
+  const int lane = threadIdx.x & 63;
+  int64_t o0 = 0, Lb = 0, cols = 0, inc = 0;
+  int64_t C;
+  if (one_chunk) {
+    if (lane < a.B) {
+      o0 = a.prefix_offsets[lane];
+      Lb = max<int64_t>(a.prefix_offsets[lane + 1] - o0, 0);
+      cols = (int64_t)c.nb * ((Lb + KT - 1) / KT + c.ntt);
+    }
+    inc = cols;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t y = __shfl_up(inc, d);
+      if (lane >= d) inc += y;
+    }
+    C = uniform64(__shfl(inc, 63));
+  } else {
+    C = uniform64(band_columns_total(a.prefix_offsets, a.B, c.nb, c.ntt));
+  }
   // at least kBandMinWindowColumns columns a window (bounds the pieces per band,
   // and so the partial traffic, and keeps every window non-empty)
   const int windows = (int)min<int64_t>(a.band_windows, max<int64_t>(1, C / kBandMinWindowColumns));
@@ -460,12 +485,29 @@ __device__ PieceCursor band_cursor_start(const AttnArgs& a, int n_rb, int block)
   c.X0 = c.win < windows ? window_edge(C, c.win, windows) : C;
   c.X1 = c.win < windows ? window_edge(C, c.win + 1, windows) : C;
   int64_t S;
-  c.b = __builtin_amdgcn_readfirstlane(band_find(a.prefix_offsets, a.B, c.nb, c.ntt, c.X0, S));
-  c.S = uniform64(S);
   c.k = 0;
   c.Tb = 1;
+  c.p0 = 0;
+  c.L = 0;
+  if (one_chunk) {
+    const unsigned long long hit = __ballot(lane < a.B && inc > c.X0);
+    c.b = __builtin_amdgcn_readfirstlane(hit ? (int)__builtin_ctzll(hit) : a.B);
+    S = C;
+    if (c.b < a.B) {
+      S = __shfl(inc - cols, c.b);
+      c.p0 = uniform64(__shfl(o0, c.b));
+      c.L = uniform64(__shfl(Lb, c.b));
+    }
+  } else {
+    c.b = __builtin_amdgcn_readfirstlane(band_find(a.prefix_offsets, a.B, c.nb, c.ntt, c.X0, S));
+    if (c.b < a.B) {
+      c.p0 = a.prefix_offsets[c.b];
+      c.L = max<int64_t>(a.prefix_offsets[c.b + 1] - c.p0, 0);
+    }
+  }
+  c.S = uniform64(S);
   if (c.b < a.B) {
-    c.Tb = band_tiles(a.prefix_offsets, c.b, c.ntt);
+    c.Tb = (int)((c.L + KT - 1) / KT) + c.ntt;
     c.k = (int)((c.X0 - c.S) / c.Tb);
   }
   // Workgroup (window x > 0, slot 0) describes edge x for the combine kernel:
@@ -505,7 +547,11 @@ __device__ __forceinline__ void band_cursor_next(const AttnArgs& a, PieceCursor&
   if (++c.k < c.nb) return;
   c.k = 0;
   c.S += (int64_t)c.nb * c.Tb;
-  if (++c.b < a.B) c.Tb = band_tiles(a.prefix_offsets, c.b, c.ntt);
+  if (++c.b < a.B) {
+    c.p0 = a.prefix_offsets[c.b];
+    c.L = max<int64_t>(a.prefix_offsets[c.b + 1] - c.p0, 0);
+    c.Tb = (int)((c.L + KT - 1) / KT) + c.ntt;
+  }
 }
 
 constexpr int KRING = 4;   // K-fragment reads in flight ahead of the S^T MFMAs
@@ -549,7 +595,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
   __shared__ uint32_t s_mask[ROWS][MAXW];
   // queries of the last QREG_LDS latent k-steps (part 0) and the rotary ones (part 1), swizzled pair rows
   __shared__ __attribute__((aligned(16))) unsigned char s_qx[2 * ROWS * R_ROW];
-  __shared__ PieceCursor s_cur;
+  __shared__ PieceCursor s_cur[2];   // the current piece's cursor and the next one's
   // second bf16 term of P of one tile, per lane, in the lane's B-operand layout
   unsigned char* const s_plo = s_kv + NBUF * TILE_BYTES;
 
@@ -588,12 +634,15 @@ verify_attn_bf16_kernel(AttnArgs a) {
   const int n_rb = (n_rows + ROWS - 1) / ROWS;
   const int64_t total_rows = (int64_t)a.B * n_rows;
   // The band cursor lives in LDS between pieces, so that none of it is held in
-  // registers across the tile loop.
+  // registers across the tile loop.  Piece i reads s_cur[i & 1] and writes the
+  // next piece's cursor to s_cur[(i + 1) & 1] as soon as it is known; the next
+  // piece's first barrier orders that write before its reads.
   if (a.balanced) {
     const PieceCursor c = band_cursor_start(a, n_rb, blockIdx.x);
-    if (tid == 0) s_cur = c;
+    if (tid == 0) s_cur[0] = c;
   }
   bool single_done = false;
+  int cur_slot = 0;
 
   for (;;) {
   __syncthreads();   // the cursor is visible; every wave is done with the previous piece's LDS
@@ -602,9 +651,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
   int64_t dest0;                  // destination row of the piece's row 0
   int64_t p0, L;
   int n_pt;
-  PieceCursor nxt;
   if (a.balanced) {
-    const PieceCursor cur = uniform_cursor(s_cur);
+    const PieceCursor cur = uniform_cursor(s_cur[cur_slot]);
     int64_t bs;
     if (!band_cursor_piece(a, cur, bs)) break;
     b = cur.b;
@@ -615,10 +663,12 @@ verify_attn_bf16_kernel(AttnArgs a) {
     to_part = !(bs >= cur.X0 && be <= cur.X1);   // a piece of a band cut by a window edge
     dest0 = to_part ? (int64_t)band_part_slot(cur.win, cur.slot, cur.rbb, bs < cur.X0) * ROWS
                     : (int64_t)b * n_rows + (int64_t)rb * ROWS;
-    nxt = cur;
+    PieceCursor nxt = cur;
     band_cursor_next(a, nxt);
-    p0 = a.prefix_offsets[b];
-    L = max<int64_t>(a.prefix_offsets[b + 1] - p0, 0);
+    cur_slot ^= 1;
+    if (tid == 0) s_cur[cur_slot] = nxt;
+    p0 = cur.p0;
+    L = cur.L;
     n_pt = (int)((L + KT - 1) / KT);
     const int last_row = min(n_rows - 1, rb * ROWS + ROWS - 1);
     t1 = min(t1, n_pt + (last_row / a.H) / KT + 1);   // tree tiles this row block can see
@@ -642,16 +692,6 @@ verify_attn_bf16_kernel(AttnArgs a) {
     const int64_t row0 = (int64_t)b * n_rows + (int64_t)rb * ROWS;
     to_part = a.splits > 1;
     dest0 = to_part ? (int64_t)split * total_rows + row0 : row0;
-  }
-
-  // ---- per-row mask words (LDS) ----
-  const int W = (a.N + 31) >> 5;
-  for (int e = tid; e < ROWS * MAXW; e += 256) {
-    const int rl = e / MAXW, w = e % MAXW;
-    const int r = rb * ROWS + rl;
-    uint32_t v = 0u;
-    if (r < n_rows && w < W) v = a.mask[((int64_t)b * a.N + r / a.H) * W + w];
-    s_mask[rl][w] = v;
   }
 
   // ---- query fragments: B operand, lane (lr, g) holds Q[row lr][16 s + 8 g .. +8] ----
@@ -696,6 +736,16 @@ verify_attn_bf16_kernel(AttnArgs a) {
       lds_dma16_rotary(sqx + 1024 * j, qlb, (uint32_t)(rr * (DL * 2)), piece + QREG * 32);
       lds_dma16_rotary(sqx + ROWS * R_ROW + 1024 * j, qrb, (uint32_t)(rr * (DR * 2)), piece);
     }
+    // ---- per-row mask words (LDS), loaded while the query copies are in flight ----
+    const int W = (a.N + 31) >> 5;
+    for (int e = tid; e < ROWS * MAXW; e += 256) {
+      const int rl = e / MAXW, w = e % MAXW;
+      const int r = rb * ROWS + rl;
+      uint32_t v = 0u;
+      if (r < n_rows && w < W) v = a.mask[((int64_t)b * a.N + r / a.H) * W + w];
+      s_mask[rl][w] = v;
+    }
+
     wait_copies();   // this wave's copies have landed
     // chunk 2 s + g of row lr sits at 128 (s >> 2) + 16 ((2 (s & 3) + g) ^ (lr & 7)):
     // four lane bases, the rest immediate offsets
@@ -737,7 +787,6 @@ verify_attn_bf16_kernel(AttnArgs a) {
   for (int i = tid; i < TILE_BYTES / 16; i += 256)
     reinterpret_cast<uint4*>(s_kv + 2 * TILE_BYTES)[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
-  if (a.balanced && tid == 0) s_cur = nxt;   // read again after the next piece's first barrier
 
   for (int pass = 0; pass < 2; ++pass) {
   bool overflow = false;
@@ -844,6 +893,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
             const int st = s - VT_EARLY;
             vring[st] = load_vt(obuf, voff, voff_hi, st / (DL / 32), st % (DL / 32));
           }
+          __builtin_amdgcn_sched_barrier(0);   // each step's reads and copy stay with its MFMA
         }
       }
     } else {
