@@ -48,6 +48,9 @@ def parse():
                     help="skip the attention-only timings of workloads 3 and 4 in the default run")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times (HBM counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("ATTN_FETCH", "ATTN_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="no GPU: write the HBM-traffic file from four rocprofv3 --pmc output folders (FETCH_SIZE and "
+                         "WRITE_SIZE of the default workload's attention, then of --copy-calibration-mb 1024)")
     return ap.parse_args()
 
 
@@ -61,6 +64,65 @@ def copy_calibration(mib, steps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": steps}), flush=True)
+
+
+def summarize_traffic(dirs, copy_mib=1024, out_path=TRAFFIC_FILE):
+    """HBM bytes per launch of the attention kernel from rocprofv3 --pmc runs: each counter's per-dispatch value
+    (KiB) averaged over the kernel's dispatches, scaled by copy bytes / the same counter's reading for the plain copy
+    of known size.  Writes out_path (the file the bench line reads), keyed to this kernel source's code hash and the
+    workload's flops."""
+    import csv
+    import glob
+
+    import numpy as np
+
+    from synth import make_config
+
+    def mean_counter(d, name):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        with open(files[0]) as f:
+            vals = [float(r["Counter_Value"]) for r in csv.DictReader(f) if name in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no {name} dispatch in {files[0]}")
+        return sum(vals) / len(vals), len(vals)
+
+    fetch, nf = mean_counter(dirs[0], ATTN_KERNEL)
+    write, nw = mean_counter(dirs[1], ATTN_KERNEL)
+    cfetch, _ = mean_counter(dirs[2], "copyBuffer")
+    cwrite, _ = mean_counter(dirs[3], "copyBuffer")
+    copy_kib = copy_mib * 1024.0
+    fs, ws = copy_kib / cfetch, copy_kib / cwrite
+    w = make_config(5)
+    depth = np.zeros_like(w.parents)
+    for i in range(1, w.N):
+        depth[:, i] = depth[np.arange(w.B), w.parents[:, i]] + 1
+    flops, _, _ = algorithmic_work(w, depth)
+    base = "rocprofv3 --pmc {c} -d <dir> -o {o} --output-format csv -- python3 bench.py {a}"
+    attn = "--steps 2 --warmup 1 --cpu-seconds 0 --no-other-workloads"
+    copy = f"--copy-calibration-mb {copy_mib} --steps 3"
+    out = {
+        "kernel": ATTN_KERNEL,
+        "workload": "k2-long-context-accept (B4 N128 H64 Dl512 Dr64 L131072)",
+        "source_sha256_16": source_hash(ATTN_SOURCE),
+        "launch_flops": int(flops),
+        "fetch_kib_per_launch_raw": fetch, "write_kib_per_launch_raw": write, "dispatches": [nf, nw],
+        "copy_calibration": {"copy_bytes": copy_mib << 20, "fetch_kib_raw": cfetch, "write_kib_raw": cwrite,
+                             "fetch_scale": round(fs, 5), "write_scale": round(ws, 5)},
+        "hbm_bytes_per_launch": int(round((fetch * fs + write * ws) * 1024)),
+        "commands": [base.format(c="FETCH_SIZE", o="bench", a=attn), base.format(c="WRITE_SIZE", o="bench", a=attn),
+                     base.format(c="FETCH_SIZE", o="copy", a=copy), base.format(c="WRITE_SIZE", o="copy", a=copy),
+                     "python3 bench.py --summarize-traffic <attn FETCH dir> <attn WRITE dir> <copy FETCH dir> "
+                     "<copy WRITE dir>"],
+        "source_hash_rule": "sha256 of the kernel source with comments, blank lines and whitespace runs removed "
+                            "(bench.py source_hash)",
+    }
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps({"hbm_bytes_per_launch": out["hbm_bytes_per_launch"], "file": out_path}))
+    return out
 
 
 def source_hash(path):
@@ -322,6 +384,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb, args.steps)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
         return
     import numpy as np
     import torch

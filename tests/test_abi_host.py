@@ -354,6 +354,28 @@ def test_bench_traffic_hash_ignores_comments_only(tmp_path):
     assert bench.source_hash(str(src)) != h0
 
 
+def test_bench_traffic_summary_from_counter_files(tmp_path):
+    """The HBM-traffic file is built from rocprofv3 --pmc outputs: per-dispatch KiB averaged over the attention
+    kernel's dispatches, scaled by the copy's bytes over the copy's reading of the same counter."""
+    import bench
+    header = '"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"\n'
+    dirs = []
+    for name, rows in (("f", [("k", bench.ATTN_KERNEL, 100.0), ("k", bench.ATTN_KERNEL, 300.0), ("o", "other", 5.0)]),
+                       ("w", [("k", bench.ATTN_KERNEL, 50.0)]),
+                       ("cf", [("c", "__amd_rocclr_copyBuffer", 512.0)]),
+                       ("cw", [("c", "__amd_rocclr_copyBuffer", 1024.0)])):
+        d = tmp_path / name / "host"
+        d.mkdir(parents=True)
+        (d / "x_counter_collection.csv").write_text(
+            header + "".join(f'1,"{k}","C",{v}\n' for _, k, v in rows))
+        dirs.append(str(tmp_path / name))
+    out = bench.summarize_traffic(dirs, copy_mib=1, out_path=str(tmp_path / "t.json"))
+    # copy of 1 MiB = 1024 KiB: fetch scale 1024 / 512 = 2, write scale 1; (200 * 2 + 50) KiB
+    assert out["copy_calibration"]["fetch_scale"] == 2.0 and out["copy_calibration"]["write_scale"] == 1.0
+    assert out["hbm_bytes_per_launch"] == (200 * 2 + 50) * 1024
+    assert out["source_sha256_16"] == bench.source_hash(bench.ATTN_SOURCE)
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py measures one GPU; --gpus above 1 exits with status 2 and a message, before touching a GPU."""
     import subprocess
