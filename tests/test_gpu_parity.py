@@ -410,6 +410,39 @@ def test_attn_bf16_slot_major_short_windows(case):
     print(f"slot-major {case}: normwise o err {eo:.2e}, lse err {el:.2e}")
 
 
+@pytest.mark.parametrize("case", [
+    dict(B=1, N=64, H=64, prefix=("fixed", 4096), splits=0),          # band schedule: 8 records per row
+    dict(B=2, N=32, H=16, prefix=("list", [1000, 300]), splits=0),    # small bands cut by window edges
+    dict(B=1, N=24, H=64, prefix=("fixed", 2000), splits=3),          # uniform splits
+])
+@pytest.mark.parametrize("e", [60, -60])
+def test_attn_bf16_partial_records_hold_any_range(case, e):
+    """Latent cache (prefix and tree rows) times 2^e and latent queries times 2^-e leave every score bit for bit
+    (power-of-two scalings are exact in bf16 and in each product), so o must come out 2^e times the unscaled o
+    and lse unchanged.  At e = +-60 the outputs lie far outside fp16's range, so this pins the partial records'
+    per-row power-of-two scale.  lse is bitwise equal; o within 1e-5 normwise: a record's log2 weight k (the
+    row's reference plus its scale exponent, |k| up to about 64 + 14 + |reference| here) is a float rounded to
+    half an ulp, 2^-18 between 64 and 128, which moves the record's weight by ln 2 * 2^-18 = 2.6e-6 relative."""
+    params = dict(K2)
+    shape = {k: v for k, v in case.items() if k != "splits"}
+    splits = case["splits"]
+    params.update(tree=("bounded", 8, 4), **shape)
+    w = make_workload(seed=61, **params)
+    dw = DevWorkload(w)
+    mask, _, _, _ = dw.build_mask()
+    o0, l0 = dw.attn(mask, num_splits=splits)
+    dw.ckv.mul_(2.0 ** e)
+    dw.ckv_tree.mul_(2.0 ** e)
+    dw.q_lat.mul_(2.0 ** -e)
+    o1, l1 = dw.attn(mask, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l0)
+    ref = o0.double() * 2.0 ** e
+    err = float((o1.double() - ref).norm() / ref.norm())
+    assert bool(torch.isfinite(o1).all()) and err <= 1e-5, err
+    print(f"records at 2^{e}, {case}: normwise o error against the exact scaling {err:.2e}")
+
+
 @pytest.mark.parametrize("H,max_len", [(8, 0), (8, 100), (64, 0)])
 def test_attn_bf16_band_understated_max_prefix_len(H, max_len):
     """The band schedule's window count is bounded on the host from max_prefix_len and on the
