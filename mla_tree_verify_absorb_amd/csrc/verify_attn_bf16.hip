@@ -81,6 +81,7 @@ constexpr int C_LOADS_PER_WAVE = KT / NWAVES;   // 8 latent rows (1 KB each) per
 constexpr int LOADS_PER_WAVE = C_LOADS_PER_WAVE + 1;  // + one 1 KB slice of the rotary region
 constexpr int MAXW = 8;                     // mask words per row (N <= 256)
 constexpr float kHeadroomLog2 = 100.0f;     // scores may exceed a row's reference by 2^100
+constexpr int kTwoTermMinFullTiles = 8;     // pieces with this many full prefix tiles take single P terms
 constexpr int kPartialTopExp = 14;          // partial records: a row's largest |value| in [2^13, 2^14)
 constexpr bf16x2 kBf16Ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -780,6 +781,12 @@ verify_attn_bf16_kernel(AttnArgs a) {
   float m_max = -INFINITY;   // true max of the scores seen, log2 units
   float l_run = 0.f;         // this lane's half of the row's exp-sum
   const float c_log2 = a.scale * 1.4426950408889634f;
+  // The second bf16 term of P (slow-path tiles) serves rows that see only a few
+  // keys.  A piece with kTwoTermMinFullTiles or more full prefix tiles gives every
+  // row at least that many tiles of keys, and single terms (as on the fast path)
+  // then suffice on its slow tiles too.
+  const int64_t full_end = min<int64_t>((int64_t)t1, L / KT);
+  const bool two_term = full_end - t0 < kTwoTermMinFullTiles;
 
   // Ring slot 2 starts zeroed: the first PV of a pass runs on it with a zero P
   // (once every wave has read its queries out of the ring).
@@ -959,7 +966,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
         // tile, a row's first visible tile) hold every key of the rows that see
         // only a few, where a single bf16 term would leave a 2^-9 relative
         // error uncancelled.
-        {
+        if (two_term) {
           bf16x8 lo[2];
 #pragma unroll
           for (int e = 0; e < 16; e += 2) {
@@ -974,8 +981,8 @@ verify_attn_bf16_kernel(AttnArgs a) {
           bf16x8* pl = reinterpret_cast<bf16x8*>(s_plo + (wave * 64 + lane) * 32);
           pl[0] = lo[0];
           pl[1] = lo[1];
+          lo_n = true;
         }
-        lo_n = true;
       }
     } else {
       // nothing after this tile: the shadow work below evaluates to p = 0
