@@ -1153,15 +1153,18 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const _Float16* __res
 }
 
 // Band schedule: merge the pieces of every band cut by a window edge.
-// Workgroup (pair p, group g) takes edge e = 1 + p / R and slot j = p % R (R row
-// blocks per band): if the band at edge e is cut there first (the attention
+// Workgroup (pair p, group g) takes edge e = 1 + p / R and slot j = p % R (R = 32
+// row blocks per band): if the band at edge e is cut there first (the attention
 // kernel's descriptor), rows 8 g .. 8 g + 7 of its row block j, from the tail
 // piece of window e - 1 and the head pieces of windows e .. last (no window is
-// empty).  32 threads per row, fp16 chunks c0 and c0 + 32 each; lane i of a row
-// reads the records of pieces i, i + 32, ..., so the weights need no serial loads.
+// empty).  With 32 row blocks a band there are at most 256 / 32 = 8 windows, so
+// at most 8 pieces: 32 threads per row, lane i < 8 loads piece i's {lse2, k},
+// and every lane loads its fp16 chunks c0 and c0 + 32 of all the pieces in the
+// same round trip (the loads do not wait for the weights).
 constexpr int kCombineRowsPerGroup = 8;
 constexpr int kCombineGroups = ROWS / kCombineRowsPerGroup;
-constexpr int kCombinePiecesInFlight = 8;   // 2 chunk loads each
+constexpr int kCombineMaxPieces = kBandWorkgroups / kBandRowBlocks;   // 8
+constexpr int kCombinePiecesInFlight = 8;   // the split kernel: pieces per wave in flight, 2 chunk loads each
 
 __device__ __forceinline__ void store_merged_row(const AttnArgs& a, int64_t grow, int c0, const float4 (&acc)[2][2],
                                                  float wsum, float mx) {
@@ -1179,7 +1182,7 @@ __device__ __forceinline__ void store_merged_row(const AttnArgs& a, int64_t grow
 
 __global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
   const int n_rows = a.N * a.H;
-  const int rbb = band_row_blocks((n_rows + ROWS - 1) / ROWS);
+  const int rbb = kBandRowBlocks;
   const int windows = reinterpret_cast<const int4*>(a.band_edges)[0].z;
   const int p = (int)blockIdx.x / kCombineGroups;
   const int grp = (int)blockIdx.x % kCombineGroups;
@@ -1195,46 +1198,38 @@ __global__ void __launch_bounds__(256) attn_band_combine_kernel(AttnArgs a) {
   const int c0 = threadIdx.x & 31;
   const _Float16* part = static_cast<const _Float16*>(a.part_o);
   auto piece_rec = [&](int i) { return (int64_t)band_part_slot(e - 1 + i, j, rbb, i > 0) * ROWS + rl; };
-  float mx = -INFINITY;
-  for (int i = c0; i < n_pc; i += 32) mx = fmaxf(mx, a.part_aux[piece_rec(i)].x);
+  float2 ax = make_float2(-INFINITY, -INFINITY);
+  if (c0 < n_pc) ax = a.part_aux[piece_rec(c0)];
+  f16x8 v[kCombineMaxPieces][2];
 #pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
-  float wsum = 0.f;
+  for (int u = 0; u < kCombineMaxPieces; ++u) {
+    if (u < n_pc) {   // uniform in the workgroup
+      const f16x8* src = reinterpret_cast<const f16x8*>(part + piece_rec(u) * DL);
+      v[u][0] = src[c0];
+      v[u][1] = src[c0 + 32];
+    }
+  }
+  float mx = ax.x;
+#pragma unroll
+  for (int off = 4; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+  mx = __shfl(mx, 0, 32);
+  // an empty piece (lse2 -inf) has weight 0 (its stored values are 0)
+  const bool live = c0 < n_pc && mx != -INFINITY;
+  const float wl = live ? exp2f(ax.x - mx) : 0.f;
+  const float wk = live ? exp2f(ax.y - mx) : 0.f;
+  float wsum = wl;
+#pragma unroll
+  for (int off = 4; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 32);
+  wsum = __shfl(wsum, 0, 32);
   float4 acc[2][2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) acc[h][0] = acc[h][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (mx != -INFINITY) {
-    for (int i0 = 0; i0 < n_pc; i0 += 32) {
-      // an empty piece (lse2 -inf) has weight 0 (its stored values are 0)
-      float wl = 0.f, wk = 0.f;
-      if (i0 + c0 < n_pc) {
-        const float2 ax = a.part_aux[piece_rec(i0 + c0)];
-        wl = exp2f(ax.x - mx);
-        wk = exp2f(ax.y - mx);
-      }
-      float ws = wl;
 #pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 32);
-      wsum += ws;
-      const int n = min(32, n_pc - i0);
-      // kCombinePiecesInFlight pieces at a time; a piece past the end re-reads piece ii with weight 0
-      for (int ii = 0; ii < n; ii += kCombinePiecesInFlight) {
-        float w[kCombinePiecesInFlight];
-        f16x8 v[kCombinePiecesInFlight][2];
-#pragma unroll
-        for (int u = 0; u < kCombinePiecesInFlight; ++u) {
-          const bool ok = ii + u < n;
-          w[u] = ok ? __shfl(wk, ii + u, 32) : 0.f;
-          const f16x8* src = reinterpret_cast<const f16x8*>(part + piece_rec(i0 + (ok ? ii + u : ii)) * DL);
-          v[u][0] = src[c0];
-          v[u][1] = src[c0 + 32];
-        }
-#pragma unroll
-        for (int u = 0; u < kCombinePiecesInFlight; ++u) {
-          partial_chunk_fma(acc[0], w[u], v[u][0]);
-          partial_chunk_fma(acc[1], w[u], v[u][1]);
-        }
-      }
+  for (int u = 0; u < kCombineMaxPieces; ++u) {
+    if (u < n_pc) {
+      const float w = __shfl(wk, u, 32);
+      partial_chunk_fma(acc[0], w, v[u][0]);
+      partial_chunk_fma(acc[1], w, v[u][1]);
     }
   }
   store_merged_row(a, (int64_t)b * n_rows + r, c0, acc, wsum, mx);
