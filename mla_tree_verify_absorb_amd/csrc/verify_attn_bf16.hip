@@ -16,7 +16,9 @@
 //    workgroup of 4 waves owns 128 rows; each wave 32 rows.
 //  * The 32 rows' absorbed queries stay in VGPRs for the whole kernel (28
 //    bf16x8 B-fragments, 112 VGPRs); the last 4 latent and the 4 rotary
-//    k-steps are staged in LDS and read per tile.
+//    k-steps are staged in LDS and read per tile.  A piece starts by copying
+//    its queries into LDS with coalesced direct-to-LDS loads and reading the
+//    fragments from there.
 //  * KV tiles of 32 keys x 576 bf16 are copied HBM -> LDS with direct-to-LDS
 //    16-byte loads into a 3-deep ring, with a 16-byte-chunk XOR swizzle that
 //    keeps both read patterns below bank-conflict free.
@@ -49,8 +51,9 @@
 //    word per row per tree tile.
 //  * Scheduling: the band schedule (below) balances ragged batches over the
 //    CUs and keeps each XCD on one KV stream; otherwise long prefixes can be
-//    split uniformly across workgroups (flash-decoding).  Partials are merged
-//    by a combine kernel with the log-sum-exp weights.
+//    split uniformly across workgroups (flash-decoding).  Partials are stored
+//    as fp16 records under a per-row power-of-two scale and merged by a
+//    combine kernel with the log-sum-exp weights.
 #include <cmath>
 
 #include "ddtree_internal.h"
@@ -1069,7 +1072,7 @@ verify_attn_bf16_kernel(AttnArgs a) {
     }
     if (g == 0) a.lse[dest0 + row_local] = lse;
   } else if (row_ok) {
-    // Partial record (see partial_chunk_dims): the unnormalised output in fp16,
+    // Partial record (see partial_chunk_dim): the unnormalised output in fp16,
     // scaled by 2^(14 - e) so that the row's largest magnitude lies in [2^13,
     // 2^14), and {lse2, k} in log2 units: the piece adds 2^lse2 to the merged
     // exp-sum and 2^k times the stored values to the merged numerator.
