@@ -1,8 +1,10 @@
-"""The hot path captured in a HIP graph: mask, tree-verify attention (band schedule and its
-merge), greedy accept.  The library allocates nothing, issues no memset and never
-synchronises, so one verify step can be captured once and replayed.  Every replay, with the
-program's own eager work and synchronisations in between, must reproduce the eager results
-bit for bit (the kernels use no atomics whose order could vary)."""
+"""GPU: the verify step (mask, attention, greedy accept) captured once in a HIP graph and replayed.
+
+Every entry point only enqueues kernels on the caller's stream (no allocation, no memset inside), so a serving
+loop can capture a step and replay it; the no-allocation attention entry point covers callers that cannot hand
+over a workspace either.  The graph holds every output buffer.  Between replays the test changes the inputs in
+place with eager work and synchronizes, then checks each replay bit for bit against eager calls on the same
+inputs, and checks that the replay followed the change."""
 import numpy as np
 import pytest
 import torch
@@ -13,66 +15,89 @@ from synth import make_workload
 
 pytestmark = pytest.mark.gpu
 
-K2 = dict(H=64, Dl=512, Dr=64, dtype="bf16", std=0.5, scale=1.0 / np.sqrt(192.0))
+K2 = dict(Dl=512, Dr=64, dtype="bf16", std=0.5, scale=1.0 / np.sqrt(192.0))
 
 
-@pytest.mark.parametrize("heads", [64, 8])
-def test_verify_step_graph_replays_match_eager(heads):
-    """64 heads: bands of 32 row blocks over 8 windows; 8 heads: bands of 4 row blocks over 19
-    windows, the band of the 3000-token request cut at several edges."""
-    params = dict(K2)
-    params.update(B=4, N=64, H=heads, prefix=("list", [500, 3000, 0, 1200]), tree=("bounded", 8, 4), V=4096,
-                  p_match=0.8)
-    w = make_workload(seed=41, **params)
+@pytest.mark.parametrize("noalloc", [True, False])
+def test_verify_step_replays_in_a_hip_graph(noalloc):
+    # 64 nodes x 64 heads: bands of 32 row blocks cut by window edges (partial records and their merge)
+    w = make_workload(B=2, N=64, H=64, prefix=("list", [3000, 700]), tree=("bounded", 8, 4), seed=81, **K2)
     dw = DevWorkload(w)
-    B, N, H = w.B, w.N, w.H
-    dev = "cuda"
+    dev = dw.q_lat.device
+    B, N, H, V = w.B, w.N, w.H, 4096
+    gen = torch.Generator().manual_seed(82)
+    logits = torch.randn((B, N, V), generator=gen).to(dev)
+    # drafts that follow the parent's argmax on 80% of the nodes, so that paths of several nodes get accepted
+    parents_l = dw.parents.long().clamp(min=0)
+    follow = logits.argmax(-1).gather(1, parents_l).int()
+    other = torch.randint(0, V, (B, N), generator=gen, dtype=torch.int32).to(dev)
+    tokens = torch.where(torch.rand((B, N), generator=gen).to(dev) < 0.8, follow, other).contiguous()
+
     W = (N + 31) // 32
-    assert dd.ddtree_verify_attn_auto_splits(dd.DDTREE_BF16, B, N, H, w.Dl, w.Dr, dw.max_len) == 0
+    mask = torch.empty((B, N, W), dtype=torch.int32, device=dev)
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    pos = torch.empty((B, N), dtype=torch.int64, device=dev)
+    ok = torch.empty((B,), dtype=torch.int32, device=dev)
+    o = torch.empty((B, N, H, w.Dl), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, N, H), dtype=torch.float32, device=dev)
     need = dd.ddtree_verify_attn_workspace_size(dd.DDTREE_BF16, B, N, H, w.Dl, w.Dr, dw.max_len, 0)
-    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
-    bufs = dict(mask=torch.empty((B, N, W), dtype=torch.int32, device=dev),
-                depth=torch.empty((B, N), dtype=torch.int32, device=dev),
-                positions=torch.empty((B, N), dtype=torch.int64, device=dev),
-                tree_ok=torch.empty((B,), dtype=torch.int32, device=dev),
-                o=torch.empty((B, N, H, w.Dl), dtype=torch.float32, device=dev),
-                lse=torch.empty((B, N, H), dtype=torch.float32, device=dev),
-                ta=torch.empty((B, N), dtype=torch.int32, device=dev),
-                al=torch.empty((B,), dtype=torch.int32, device=dev),
-                an=torch.empty((B, N), dtype=torch.int32, device=dev),
-                ct=torch.empty((B, N), dtype=torch.int32, device=dev))
+    assert need > 0
+    ws = None if noalloc else torch.empty((need,), dtype=torch.uint8, device=dev)
+    targ = torch.empty((B, N), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    commit = torch.empty((B, N), dtype=torch.int32, device=dev)
+    outputs = (mask, depth, pos, ok, o, lse, targ, alen, nodes, commit)
 
     def step():
-        dd.ddtree_build_mask(dw.parents, dw.offsets, mask=bufs["mask"], depth=bufs["depth"],
-                             positions=bufs["positions"], tree_ok=bufs["tree_ok"])
-        dd.ddtree_verify_attn(dw.q_lat, dw.q_rope, dw.ckv, dw.krope, dw.offsets, dw.max_len, dw.ckv_tree,
-                              dw.krope_tree, bufs["mask"], w.scale, num_splits=0, o=bufs["o"], lse=bufs["lse"],
-                              workspace=ws)
-        dd.ddtree_greedy_accept(dw.logits, dw.tokens, dw.parents, target_argmax=bufs["ta"], accept_len=bufs["al"],
-                                accept_nodes=bufs["an"], commit_tokens=bufs["ct"])
+        dd.ddtree_build_mask(dw.parents, dw.offsets, mask=mask, depth=depth, positions=pos, tree_ok=ok)
+        args = (dw.q_lat, dw.q_rope, dw.ckv, dw.krope, dw.offsets, dw.max_len, dw.ckv_tree, dw.krope_tree, mask,
+                w.scale)
+        if noalloc:
+            dd.ddtree_verify_attn_noalloc(*args, o=o, lse=lse)
+        else:
+            dd.ddtree_verify_attn(*args, o=o, lse=lse, workspace=ws)
+        dd.ddtree_greedy_accept(logits, tokens, dw.parents, target_argmax=targ, accept_len=alen, accept_nodes=nodes,
+                                commit_tokens=commit)
 
-    step()
+    # warm-up on a side stream (the first no-allocation call looks up the scratch address), then capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    eager = {k: v.clone() for k, v in bufs.items()}
-
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step()                                   # warm up on the capture stream
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
 
-    for replay in range(3):
-        for v in bufs.values():                  # eager work between replays: clobber every output
-            v.fill_(-7)
-        ws.fill_(0xAB)
+    prev = None
+    for rep in range(4):
+        if rep == 1:
+            dw.q_lat.mul_(0.5)                              # exact in bf16: every score halves
+        elif rep == 2:
+            logits.copy_(torch.roll(logits, 1, dims=2))     # every row's argmax moves by one
+        elif rep == 3:
+            dw.ckv_tree.mul_(2.0)                           # the tree rows' latent keys and values change
         torch.cuda.synchronize()
-        g.replay()
+        for t in outputs:
+            t.fill_(-7)
+        graph.replay()
         torch.cuda.synchronize()
-        for k, v in bufs.items():
-            assert torch.equal(v, eager[k]), f"replay {replay}: {k} differs from the eager step"
-    print(f"3 replays bitwise equal to eager; accept_len {eager['al'].tolist()}")
+        got = [t.clone() for t in outputs]
+        step()
+        torch.cuda.synchronize()
+        eager = [t.clone() for t in outputs]
+        for i, (a, b) in enumerate(zip(got, eager)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager call"
+        assert int(ok.min()) == 1 and bool(torch.isfinite(o).all())
+        if rep == 0:
+            first_alen = got[7].tolist()
+            assert max(first_alen) >= 1                     # the accept path is exercised
+        if prev is not None:
+            changed = {1: [4, 5], 2: [6], 3: [4]}[rep]      # o/lse; target argmax; o
+            for i in changed:
+                assert not torch.equal(got[i], prev[i]), f"replay {rep}: output {i} did not follow its input"
+        prev = got
+    print(f"graph replays (noalloc={noalloc}): accept lengths {first_alen}, then {alen.tolist()} after the logits moved")
