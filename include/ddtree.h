@@ -293,7 +293,10 @@ int ddtree_compact_kv(int32_t dtype, int32_t B, int32_t N, int32_t Dl, int32_t D
  * parent index, proposal rank ascending) until N nodes exist and are numbered
  * in that order, so parents precede children and the output is a valid tree
  * for ddtree_build_mask.  With log-probabilities <= 0 the result is the root
- * plus the N-1 best nodes of the whole candidate tree under that key.
+ * plus the N-1 best nodes of the whole candidate tree under that key.  The
+ * ordering along K is a precondition (the kernel offers a node's proposals to
+ * the frontier one rank at a time): with proposals out of order the result is
+ * still a valid tree of N nodes, but not necessarily the best-first one.
  *
  *   B, N             requests (>= 0), nodes per tree (1 .. DDTREE_MAX_NODES)
  *   D, K             draft depths (1 .. DDTREE_MAX_DEPTH) and proposals per depth
