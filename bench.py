@@ -259,10 +259,11 @@ def time_rope(dd, torch, w, dev, q_rope, kv_tree, positions, steps):
     return {"us_per_call": us, "rows": rows, "bytes_moved": 2 * rows * w.Dr * q_rope.element_size()}
 
 
-def reference_rates(torch, dev):
-    """Rates this GPU attains on plain library work, as context for the vendor peaks: a large dense bf16 GEMM
-    (torch.matmul, hipBLASLt) and a plain 1 GiB device-to-device copy (read + write bytes).  Neither is part of
-    the verify path."""
+def reference_rates(torch, dev, accept_bytes=0):
+    """Rates this GPU attains on plain work, as context for the vendor peaks: a large dense bf16 GEMM
+    (torch.matmul, hipBLASLt), a plain 1 GiB device-to-device copy (read + write bytes), and the library's own
+    probes: back-to-back bf16 MFMAs, and a read-only stream of 2 GiB and of the accept call's logits size (the
+    best of three workgroup counts each).  None is part of the verify path."""
     n = 8192
     a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
     b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
@@ -287,17 +288,20 @@ def reference_rates(torch, dev):
 
     gemm_ms = best_ms(lambda: torch.matmul(a, b, out=c))
     copy_ms = best_ms(lambda: y.copy_(x))
-    # the library's own probes: back-to-back bf16 MFMAs on every SIMD, and a read-only stream of 2 GiB
+    # the library's own probes: back-to-back bf16 MFMAs on every SIMD, and read-only streams
     from mla_tree_verify_absorb_amd import rates
     wgs, iters = 512, 40000                       # two waves per SIMD on 256 CUs
     sink = torch.empty((wgs * 4,), dtype=torch.float32, device=dev)
     mfma_flops = rates.mfma_loop(wgs, iters, sink)
     mfma_ms = best_ms(lambda: rates.mfma_loop(wgs, iters, sink), reps=5)
-    rd_wgs = 256 * 8
-    rsink = torch.empty((rd_wgs * 256,), dtype=torch.int32, device=dev)
+    rd_counts = (1024, 2048, 4096)
+    rsink = torch.empty((max(rd_counts) * 256,), dtype=torch.int32, device=dev)
     buf = torch.ones(((2 << 30) // 4,), dtype=torch.float32, device=dev)
-    rd_bytes = rates.stream_read(buf, rd_wgs, rsink)
-    rd_ms = best_ms(lambda: rates.stream_read(buf, rd_wgs, rsink))
+
+    def best_stream(nbytes):
+        view = buf[: nbytes // 4]
+        rd_ms = min(best_ms(lambda: rates.stream_read(view, g, rsink)) for g in rd_counts)
+        return round(nbytes / (rd_ms * 1e-3) / 1e9, 1)
     out = {"gemm_bf16_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
            "gemm_shape": [n, n, n],
            "copy_gbps": round(2 * x.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1),
@@ -305,8 +309,13 @@ def reference_rates(torch, dev):
            "mfma_loop_bf16_tflops": round(mfma_flops / (mfma_ms * 1e-3) / 1e12, 1),
            "mfma_loop": f"{wgs} workgroups x 4 waves, {iters} iterations of 4 independent "
                         f"v_mfma_f32_32x32x16_bf16 per wave, median of 5",
-           "stream_read_gbps": round(rd_bytes / (rd_ms * 1e-3) / 1e9, 1),
-           "stream_read_bytes": rd_bytes}
+           "stream_read_gbps": best_stream(buf.numel() * 4),
+           "stream_read_bytes": buf.numel() * 4,
+           "stream_read": f"contiguous spans per workgroup, 8 nontemporal 16-byte loads in flight per thread, "
+                          f"best of {list(rd_counts)} workgroups of 256 threads"}
+    if 0 < accept_bytes <= buf.numel() * 4 and accept_bytes % 16 == 0:
+        out["stream_read_accept_size_gbps"] = best_stream(accept_bytes)
+        out["stream_read_accept_size_bytes"] = accept_bytes
     del a, b, c, x, y, buf
     return out
 
@@ -501,12 +510,15 @@ def main():
     if args.config == 5 and args.heads == 0 and args.splits == 0 and not args.no_other_workloads:
         out["other_workloads"] = {CONFIGS[k]["name"]: attention_only(dd, torch, dev, k, args.steps, args.warmup)
                                   for k in (3, 4)}
-    ref = reference_rates(torch, dev)
+    ref = reference_rates(torch, dev, accept_bytes)
     roofline["frac_of_measured_gemm"] = round(attn_tflops / ref["gemm_bf16_tflops"], 4)
     roofline["frac_of_measured_mfma_loop"] = round(attn_tflops / ref["mfma_loop_bf16_tflops"], 4)
     if accept_bytes:
         out["accept_frac_of_measured_copy"] = round(out["accept_hbm_gbps"] / ref["copy_gbps"], 4)
         out["accept_frac_of_measured_stream_read"] = round(out["accept_hbm_gbps"] / ref["stream_read_gbps"], 4)
+        if "stream_read_accept_size_gbps" in ref:
+            out["accept_frac_of_same_size_stream_read"] = round(
+                out["accept_hbm_gbps"] / ref["stream_read_accept_size_gbps"], 4)
     for sub in out.get("other_workloads", {}).values():
         sub["frac_of_measured_mfma_loop"] = round(sub["attn_tflops"] / ref["mfma_loop_bf16_tflops"], 4)
     out["reference_rates"] = ref

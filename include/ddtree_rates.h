@@ -26,7 +26,9 @@ int ddtree_rates_mfma_loop(int32_t workgroups, int32_t iters, float* sink, void*
 int64_t ddtree_rates_mfma_loop_flops(int32_t workgroups, int32_t iters);
 
 /* Read-only HBM stream: reads `bytes` (a multiple of 16, 16-byte aligned src)
- * once with 16-byte nontemporal loads.  sink: device uint32 [workgroups * 256]. */
+ * once with 16-byte nontemporal loads, each of the `workgroups` workgroups
+ * (256 threads) one contiguous span of about bytes / workgroups.
+ * sink: device uint32 [workgroups * 256]. */
 int ddtree_rates_stream_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
