@@ -225,7 +225,7 @@ def test_attn_bf16_full_configs(k):
     assert ea <= BF16_LSE_ABS_TOL, ea
 
 
-def test_attn_bf16_config3_every_row():
+def test_attn_bf16_single_request_every_row():
     """The single 64-node request over 4096 tokens, every one of its 4096 rows against the oracle: each row is
     merged from 8 fp16 partial records (one band of 32 row blocks over 8 windows, slot-major mapping)."""
     w, dw = config(3)
@@ -235,11 +235,12 @@ def test_attn_bf16_config3_every_row():
     o_ref, lse_ref = oracle_attn(w, m_ref)
     eo, el = compare_attn(w, o, lse, o_ref, lse_ref)
     ea = lse_abs_err(lse, lse_ref)
-    print(f"config 3, every row: normwise o err {eo:.2e}, lse err {el:.2e} (absolute {ea:.2e} nats)")
+    print(f"k2-single (B1 N64 H64 L4096), every row: normwise o err {eo:.2e}, lse err {el:.2e} "
+          f"(absolute {ea:.2e} nats)")
     assert ea <= BF16_LSE_ABS_TOL, ea
 
 
-def test_attn_bf16_config4_every_request():
+def test_attn_bf16_ragged_batch_every_request():
     """The ragged batch: the root, a middle node and the last node of every one of its 16 requests (prefixes
     of 1K to 32K tokens, bands cut by window edges) against the oracle."""
     w, dw = config(4)
@@ -250,7 +251,8 @@ def test_attn_bf16_config4_every_request():
     o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
     eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
     ea = lse_abs_err(lse, lse_ref, nodes=nodes)
-    print(f"config 4, every request: normwise o err {eo:.2e}, lse err {el:.2e} (absolute {ea:.2e} nats) "
+    print(f"k2-batched-ragged (B16 N64 H64), every request: normwise o err {eo:.2e}, lse err {el:.2e} "
+          f"(absolute {ea:.2e} nats) "
           f"on {len(nodes)} nodes")
     assert ea <= BF16_LSE_ABS_TOL, ea
 
