@@ -7,8 +7,8 @@
  *   DIR/meta.txt   "B N H Dl Dr V max_prefix_len cache_rows scale"
  *   DIR/*.bin      raw little-endian inputs (names below; bf16 as 16-bit words)
  * Writes the outputs as raw files into DIR and prints the library's build
- * digest.  Exit status 0 on success; any failed call prints its status string
- * and exits non-zero.
+ * digest and the hash of the source it was built from.  Exit status 0 on
+ * success; any failed call prints its status string and exits non-zero.
  *
  * Steps: ddtree_build_mask -> ddtree_verify_attn (band schedule, caller
  * workspace) -> ddtree_verify_attn_noalloc (same inputs, for comparison) ->
@@ -22,6 +22,10 @@
 #include <string.h>
 
 #include "ddtree.h"
+
+#ifndef C_ABI_STEP_SOURCE_HASH
+#define C_ABI_STEP_SOURCE_HASH "unknown"
+#endif
 
 static const char* g_dir;
 
@@ -100,6 +104,7 @@ int main(int argc, char** argv) {
   if (fscanf(mf, "%d %d %d %d %d %d %lld %lld %f", &B, &N, &H, &Dl, &Dr, &V, &max_len, &cache_rows, &scale) != 9)
     die(meta_path, "expected B N H Dl Dr V max_prefix_len cache_rows scale");
   fclose(mf);
+  printf("source %s\n", C_ABI_STEP_SOURCE_HASH);
   printf("digest %s\n", ddtree_build_digest());
   printf("case B=%d N=%d H=%d Dl=%d Dr=%d V=%d max_prefix_len=%lld cache_rows=%lld\n", B, N, H, Dl, Dr, V, max_len,
          cache_rows);

@@ -16,15 +16,12 @@ from synth import make_workload
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "tests", "c_abi_step.c")
 BIN = os.path.join(ROOT, "tests", "_build", "c_abi_step")
 
 
 def test_c_caller_runs_a_verify_step(tmp_path):
-    if not os.path.exists(BIN) or os.path.getmtime(BIN) < max(os.path.getmtime(SRC),
-                                                                os.path.getmtime(os.path.join(ROOT, "include",
-                                                                                              "ddtree.h"))):
-        pytest.fail(f"{BIN} is missing or older than its source; run __graft_entry__.build()")
+    if not os.path.exists(BIN):   # build() warns when gcc is unavailable and builds the library regardless
+        pytest.skip(f"{BIN} was not built (no C compiler when __graft_entry__.build() ran)")
     # ragged prefixes with an empty one; 40 nodes x 16 heads = 5 row blocks per request
     w = make_workload(B=3, N=40, H=16, Dl=512, Dr=64, dtype="bf16", std=0.5, scale=1.0 / np.sqrt(192.0),
                       prefix=("list", [300, 0, 77]), tree=("bounded", 8, 4), V=3000, p_match=0.7, seed=91)
@@ -48,6 +45,8 @@ def test_c_caller_runs_a_verify_step(tmp_path):
     print(res.stdout)
     assert res.returncode == 0, res.stderr
     from mla_tree_verify_absorb_amd.build import source_digest
+    from __graft_entry__ import c_driver_source_hash
+    assert f"source {c_driver_source_hash()}" in res.stdout, "stale C caller: run __graft_entry__.build()"
     assert f"digest {source_digest()}" in res.stdout            # the library built from these sources
 
     def out(name, dtype, shape):
