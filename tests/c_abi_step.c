@@ -10,7 +10,7 @@
  * digest and the hash of the source it was built from.  Exit status 0 on
  * success; any failed call prints its status string and exits non-zero.
  *
- * Steps: ddtree_build_mask -> ddtree_verify_attn (band schedule, caller
+ * Steps: ddtree_build_mask -> ddtree_verify_attn (automatic schedule, caller
  * workspace) -> ddtree_verify_attn_noalloc (same inputs, for comparison) ->
  * ddtree_greedy_accept -> ddtree_compact_kv (the accepted rows appended to the
  * cache at dest_rows).
