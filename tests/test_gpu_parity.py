@@ -257,6 +257,22 @@ def test_attn_bf16_ragged_batch_every_request():
     assert ea <= BF16_LSE_ABS_TOL, ea
 
 
+def test_attn_bf16_long_context_every_request():
+    """The 131072-token batch: two nodes of every one of its 4 requests (each request's 64 row blocks form two
+    bands, which the workgroup mapping places on their own pair of XCDs) against the oracle."""
+    w, dw = config(5)
+    mask, m_ref = check_mask(dw)
+    o, lse = dw.attn(mask)
+    torch.cuda.synchronize()
+    nodes = [(b, i) for b in range(w.B) for i in (w.N // 3, 2 * w.N // 3 + 1)]
+    o_ref, lse_ref = oracle_attn(w, m_ref, nodes=nodes)
+    eo, el = compare_attn(w, o, lse, o_ref, lse_ref, nodes=nodes)
+    ea = lse_abs_err(lse, lse_ref, nodes=nodes)
+    print(f"k2-long-context (B4 N128 H64 L131072), every request: normwise o err {eo:.2e}, lse err {el:.2e} "
+          f"(absolute {ea:.2e} nats) on {len(nodes)} nodes")
+    assert ea <= BF16_LSE_ABS_TOL, ea
+
+
 @pytest.mark.parametrize("k", [3, 4, 5])
 def test_attn_bf16_tp8_share(k):
     """One GPU's share of the K2 workloads under 8-way head parallelism (8 of 64 heads, the latent
